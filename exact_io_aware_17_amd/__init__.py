@@ -1,0 +1,23 @@
+"""MI355X-native exact attention: libfa (C-ABI, gfx950 HIP kernels) and its binding.
+
+    from exact_io_aware_17_amd import fwd, bwd
+    o, lse = fwd(q, k, v, causal=True)              # bf16 or fp32 [B, H, N, d] GPU tensors
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+
+The library is loaded on first use; importing this package touches no GPU.
+"""
+from ._lib import (  # noqa: F401
+    FA_ERR_HIP,
+    FA_ERR_INVALID_ARG,
+    FA_ERR_UNSUPPORTED,
+    FA_MASK_CAUSAL,
+    FA_MASK_NONE,
+    FA_OK,
+    FaError,
+    bwd,
+    bwd_workspace_bytes,
+    default_scale,
+    fwd,
+    load,
+    status_string,
+)

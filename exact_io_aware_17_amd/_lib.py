@@ -1,0 +1,194 @@
+"""ctypes binding of libfa (include/fa.h): argument marshalling only.
+
+Every step of the attention runs in libfa's gfx950 kernels. PyTorch supplies
+device memory (output and workspace tensors) and the current HIP stream.
+There is no fallback: if libfa.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_HIP = -3
+FA_MASK_NONE = 0
+FA_MASK_CAUSAL = 1
+ABI_VERSION = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+# Exported symbol -> (restype, argtypes), in the order include/fa.h declares them.
+SIGNATURES = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                    _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_i]),
+    "fa_abi_version": (_i, []),
+}
+
+
+class FaError(RuntimeError):
+    """A libfa call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once (after torch, so it binds to the HIP runtime torch uses)."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libfa.so not found at {path}; build it with `python -m exact_io_aware_17_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libfa ABI {lib.fa_abi_version()} != expected {ABI_VERSION}")
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != FA_OK:
+        raise FaError(fn, status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    """float32(1/sqrt(d)), the value every path receives."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape [B, H, N, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def _kv_ptr(kv_lens, B, dev):
+    if kv_lens is None:
+        return None
+    if kv_lens.dtype != torch.int32 or kv_lens.device != dev or kv_lens.shape != (B,) \
+            or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be a contiguous int32 [B] tensor on the inputs' device")
+    return kv_lens.data_ptr()
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd (bfloat16) or fa_fwd_f32 (float32). Returns (O, lse)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    if q.dtype == torch.bfloat16:
+        fn_name = "fa_fwd"
+    elif q.dtype == torch.float32:
+        fn_name = "fa_fwd_f32"
+    else:
+        raise ValueError("q, k, v must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must match q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    kvp = _kv_ptr(kv_lens, B, q.device)
+    lib = load()
+    with torch.cuda.device(q.device):
+        st = getattr(lib, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                   float(scale), FA_MASK_CAUSAL if causal else FA_MASK_NONE, kvp,
+                                   _stream(q.device))
+    _check(fn_name, st)
+    return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+        lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
+        scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """fa_bwd (bfloat16). Returns (dQ, dK, dV)."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if q.dtype != torch.bfloat16:
+        raise ValueError("fa_bwd takes bfloat16 tensors")
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must match q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = default_scale(d)
+    lib = load()
+    wsb = int(lib.fa_bwd_workspace_bytes(B, H, N, d))
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < wsb:
+        raise ValueError(f"workspace needs {wsb} bytes")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    kvp = _kv_ptr(kv_lens, B, q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, float(scale),
+                        FA_MASK_CAUSAL if causal else FA_MASK_NONE, kvp, _stream(q.device))
+    _check("fa_bwd", st)
+    return dq, dk, dv

@@ -1,0 +1,157 @@
+// Host entry points of libfa: argument validation, then one launch per step on
+// the caller's stream. Validation happens before any HIP call, so every
+// argument error is reported without touching the device.
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared checks of the shape, scale and mask arguments.
+int check_common(int B, int H, int N, int d, float scale, int mask_kind) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // Row indices (b*H + h)*N + i are formed in 32-bit arithmetic.
+  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+float scale_log2(float scale) {
+  return (float)((double)scale * 1.4426950408889634073599246810019);
+}
+
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream,
+               size_t elem, bool f32) {
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  int st = check_common(B, H, N, d, scale, mask_kind);
+  if (st != FA_OK) return st;
+  const size_t tbytes = (size_t)B * H * N * d * elem;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
+      overlaps(o, tbytes, v, tbytes))
+    return FA_ERR_INVALID_ARG;
+  if (lse && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
+              overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
+  if (kv_lens && ((uintptr_t)kv_lens & 3u)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.kv_lens = kv_lens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.scale_log2 = scale_log2(scale);
+  p.causal = (mask_kind == FA_MASK_CAUSAL);
+  hipError_t e = f32 ? fa::launch_fwd_f32(p, (hipStream_t)stream)
+                     : fa::launch_fwd_bf16(p, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: unsupported head dimension, alignment or size";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP: kernel launch failed";
+    default:
+      return "unknown fa_status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, stream, 2, false);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, stream, 4, true);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N, d);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  int st = check_common(B, H, N, d, scale, mask_kind);
+  if (st != FA_OK) return st;
+  const size_t tbytes = (size_t)B * H * N * d * 2;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const size_t wbytes = fa::bwd_workspace_bytes(B, H, N, d);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t insz[6] = {tbytes, tbytes, tbytes, tbytes, tbytes, lbytes};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outsz[4] = {tbytes, tbytes, tbytes, wbytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      ((uintptr_t)lse & 3u) || (kv_lens && ((uintptr_t)kv_lens & 3u)))
+    return FA_ERR_UNSUPPORTED;
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = (float*)workspace;
+  p.kv_lens = kv_lens;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.scale_log2 = scale_log2(scale);
+  p.causal = (mask_kind == FA_MASK_CAUSAL);
+  hipError_t e = fa::launch_bwd_bf16(p, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device-side types and helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float POS_INF = __builtin_huge_valf();
+constexpr float LN2 = 0.69314718055994530942f;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+// Physical 16-byte slot of logical chunk c in a row-major tile row of D bf16
+// (D*2 bytes). The XOR spreads 16 consecutive rows over 16 distinct slots.
+template <int D>
+__device__ __forceinline__ int row_slot(int row, int c) {
+  if constexpr (D == 128) {
+    return c ^ (row & 15);
+  } else {
+    return c ^ ((row >> 1) & 7);
+  }
+}
+
+// Physical slot of logical chunk c in a transposed tile row of 64 bf16 (128 B).
+__device__ __forceinline__ int t64_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// Position of index x inside its 16-group of a transposed tile: bits 2 and 3
+// swapped. This is the order in which a 32x32 MFMA accumulator holds the
+// rows of its C tile when they are fed back as the 8-wide contraction slots
+// of the next MFMA.
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Round two floats to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+// Lanes l and l^32 share a row; permlane32_swap hands each lane the pair
+// {x[l & 31], x[(l & 31) + 32]} in its two results, so the combinations below
+// are bitwise identical on both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Low / high bf16 of a packed word, as raw 16-bit values.
+__device__ __forceinline__ unsigned lo16(unsigned w) { return w & 0xffffu; }
+__device__ __forceinline__ unsigned hi16(unsigned w) { return w >> 16; }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void zero(f32x16& x) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = 0.f;
+}
+
+}  // namespace dev
+}  // namespace fa

@@ -1,0 +1,123 @@
+/*
+ * libfa - exact attention (FlashAttention forward and recompute backward)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed, per batch b and head h, for query row i:
+ *   S_ij  = scale * <Q_i, K_j>                       (scores; "Foundations",
+ *            sections 4 and 9: query-key dot products scaled by 1/sqrt(d_k))
+ *   S_ij  = -inf where key j is hidden                ("Worked examples", Cell D)
+ *   O_i   = sum_j softmax(S_i)_j V_j                  ("Foundations", sections 7-8)
+ *   lse_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
+ * computed by streaming K/V in blocks with the online max / normaliser
+ * recurrence and one division at the end (the interactive explainer on
+ * "The Flash Attention"; "Exercises", the block merges). Neither S nor the
+ * probabilities P = softmax(S) are ever written to device memory.
+ * A row with no visible key returns O_i = 0 and lse_i = -inf ("Worked
+ * examples", Cell D2, the guard).
+ *
+ * Visibility: key j is visible to query i iff
+ *   (mask_kind != FA_MASK_CAUSAL || j <= i)  &&  j < kv_len_b,
+ * where kv_len_b = kv_lens[b] clamped to [0, N] (kv_lens == NULL means N).
+ * Causal masking is top-left aligned (queries and keys share positions
+ * 0..N-1). Padding hides keys only; every query row is computed.
+ *
+ * Layout: every tensor is contiguous [B, H, N, d] (d innermost), lse is
+ * contiguous [B, H, N] float32. Pointers are device pointers allocated by
+ * the caller (the library allocates and frees nothing and keeps no mutable
+ * state). Tensor base pointers must be 16-byte aligned.
+ *
+ * Asynchrony: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * Faults inside a kernel surface at the caller's next synchronisation.
+ *
+ * Errors are returned before anything is enqueued:
+ *   FA_ERR_INVALID_ARG  null tensor pointer, B/H/N <= 0, scale not finite
+ *                       or not > 0, unknown mask_kind, an output overlapping
+ *                       an input;
+ *   FA_ERR_UNSUPPORTED  d not supported (64 and 128 are), a tensor pointer
+ *                       not 16-byte aligned, sizes whose element count does
+ *                       not fit the kernels' 32-bit row indices;
+ *   FA_ERR_HIP          the launch itself failed (hipGetLastError).
+ * kv_lens values outside [0, N] are clamped by the kernels.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1,
+  FA_ERR_UNSUPPORTED = -2,
+  FA_ERR_HIP = -3
+} fa_status;
+
+typedef enum {
+  FA_MASK_NONE = 0,   /* every key visible (subject to kv_lens) */
+  FA_MASK_CAUSAL = 1  /* key j visible to query i iff j <= i */
+} fa_mask_kind;
+
+/*
+ * Forward pass, bfloat16 inputs and output, float32 logsumexp.
+ *   q, k, v : [B, H, N, d] bfloat16 (read)
+ *   o       : [B, H, N, d] bfloat16 (written; round-to-nearest-even)
+ *   lse     : [B, H, N] float32 (written; natural log; -inf for empty rows);
+ *             may be NULL when the caller does not need it
+ *   scale   : multiplies Q K^T; normally 1/sqrt(d)
+ *   kv_lens : device int32 [B] valid key counts, or NULL
+ *   stream  : hipStream_t
+ * Products Q K^T and P V run on bf16 matrix cores with float32 accumulation;
+ * P is rounded to bfloat16 before the P V product.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int mask_kind,
+           const int32_t* kv_lens, void* stream);
+
+/*
+ * The same contract with float32 q, k, v, o (float32 arithmetic throughout).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int mask_kind,
+               const int32_t* kv_lens, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (caller-allocated,
+ * at least 256-byte aligned; contents need not be initialised).
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass of fa_fwd: given dO = dL/dO, returns dQ, dK, dV.
+ * P is recomputed from Q, K and the saved lse (the "Question bank" answers:
+ * S and P are recomputed rather than stored); the formulas are the standard
+ * softmax derivative:
+ *   P = exp(S - lse) (0 where hidden or lse = -inf),  D_i = sum_c dO_ic O_ic,
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dout : [B, H, N, d] bfloat16 (read); o is fa_fwd's output
+ *   lse              : [B, H, N] float32 from fa_fwd (read)
+ *   dq, dk, dv       : [B, H, N, d] bfloat16 (written)
+ *   workspace        : fa_bwd_workspace_bytes(B, H, N, d) bytes of device memory
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace,
+           int B, int H, int N, int d, float scale, int mask_kind,
+           const int32_t* kv_lens, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the library that was loaded. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

@@ -1,0 +1,59 @@
+"""Helpers shared by the GPU parity tests: run the oracle on the exact inputs
+the GPU received and compare element by element."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as orc
+
+INF = float("inf")
+
+# Tolerances (GPU vs fp64 oracle).
+F32_O = 1e-5          # fp32 inputs: max-abs on O
+F32_LSE = 1e-5
+BF16_O_MAX = 2e-2     # bf16 inputs: max-abs on O
+BF16_O_MEAN = 2e-3    # bf16 inputs: mean-abs on O
+BF16_LSE_ABS = 1e-3   # bf16: |dlse| <= 1e-3 + 1e-5 |lse|
+BF16_LSE_REL = 1e-5
+BF16_GRAD = 5e-2      # bf16 gradients: max-abs
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, abs_tol: float, rel_tol: float = 0.0):
+    """Empty rows must be exactly -inf on both sides; finite rows within tolerance."""
+    ref_empty = lse_ref == -INF
+    gpu_empty = lse_gpu == -INF
+    assert np.array_equal(ref_empty, gpu_empty), "empty-row pattern differs"
+    fin = ~ref_empty
+    if fin.any():
+        err = np.abs(lse_gpu[fin] - lse_ref[fin])
+        bound = abs_tol + rel_tol * np.abs(lse_ref[fin])
+        assert np.all(err <= bound), f"lse max err {err.max():.3g}"
+
+
+def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, max_tol: float, mean_tol: float = None):
+    assert np.all(np.isfinite(o_gpu)), "non-finite output"
+    err = np.abs(o_gpu - o_ref)
+    say(f"   O max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= max_tol, f"O max-abs {err.max():.3g} > {max_tol}"
+    if mean_tol is not None:
+        assert err.mean() <= mean_tol, f"O mean-abs {err.mean():.3g} > {mean_tol}"
+
+
+def oracle_fwd(q, k, v, scale, causal, kv_lens=None, rows=None, heads=None):
+    kv = None if kv_lens is None else [int(x) for x in kv_lens.cpu().tolist()]
+    return orc.attn_fwd_naive(to64(q), to64(k), to64(v), scale, causal, kv, rows=rows, heads=heads)
+
+
+def oracle_bwd(q, k, v, do, scale, causal, kv_lens=None):
+    kv = None if kv_lens is None else [int(x) for x in kv_lens.cpu().tolist()]
+    return orc.attn_bwd(to64(q), to64(k), to64(v), to64(do), scale, causal, kv)

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects bad
+arguments on the host before touching a device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_17_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Fake, 256-byte-aligned, non-overlapping "device" addresses: validation never
+# dereferences them, and every call below fails validation before any HIP call.
+A = 0x10000000
+SZ = 0x01000000
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_symbols() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.fa_abi_version() == _lib.ABI_VERSION
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in (0, -1, -2, -3):
+        assert lib.fa_status_string(code)
+    assert b"unknown" in lib.fa_status_string(99)
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    assert lib.fa_bwd_workspace_bytes(2, 16, 4096, 128) >= 2 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 16, 4096, 128) % 256 == 0
+    assert lib.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+
+
+def _fwd(fn="fa_fwd", q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ,
+         B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
+    lib = _lib.load()
+    return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, scale, mask, kv, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_argument_errors(fn):
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    assert _fwd(fn, q=None) == INV
+    assert _fwd(fn, o=None) == INV
+    assert _fwd(fn, B=0) == INV
+    assert _fwd(fn, H=-1) == INV
+    assert _fwd(fn, N=0) == INV
+    assert _fwd(fn, scale=float("nan")) == INV
+    assert _fwd(fn, scale=float("inf")) == INV
+    assert _fwd(fn, scale=0.0) == INV
+    assert _fwd(fn, scale=-0.125) == INV
+    assert _fwd(fn, mask=2) == INV
+    assert _fwd(fn, o=A + 8) == INV                 # output overlaps q
+    assert _fwd(fn, lse=A + SZ + 64) == INV         # lse overlaps k
+    assert _fwd(fn, d=96) == UNS
+    assert _fwd(fn, d=32) == UNS
+    assert _fwd(fn, q=A + 2) == UNS                 # not 16-byte aligned
+    assert _fwd(fn, kv=A + 5 * SZ + 2) == UNS       # kv_lens not 4-byte aligned
+    assert _fwd(fn, B=1 << 16, H=1 << 16, N=1) == UNS  # row count beyond 32-bit
+
+
+def test_bwd_argument_errors():
+    lib = _lib.load()
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    base = [A + i * SZ for i in range(10)]
+
+    def call(ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, mask=1):
+        p = list(base if ptrs is None else ptrs)
+        return lib.fa_bwd(*p, B, H, N, d, scale, mask, None, None)
+
+    for i in range(10):
+        p = list(base)
+        p[i] = None
+        assert call(p) == INV, i
+    assert call(B=0) == INV
+    assert call(scale=float("nan")) == INV
+    assert call(mask=7) == INV
+    p = list(base)
+    p[6] = base[0] + 16       # dq overlaps q
+    assert call(p) == INV
+    p = list(base)
+    p[7] = base[6]            # dk aliases dq
+    assert call(p) == INV
+    assert call(d=256) == UNS
+    p = list(base)
+    p[9] = base[9] + 8        # workspace misaligned
+    assert call(p) == UNS
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        _lib.load(str(tmp_path / "missing.so"))

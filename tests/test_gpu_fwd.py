@@ -1,0 +1,200 @@
+"""GPU parity of fa_fwd / fa_fwd_f32 against the fp64 oracle (through the C-ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_17_amd as fa
+from exact_io_aware_17_amd import workloads as W
+
+from _parity import (BF16_LSE_ABS, BF16_LSE_REL, BF16_O_MAX, BF16_O_MEAN, F32_LSE, F32_O,
+                     INF, check_lse, check_o, oracle_fwd, say, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _run(w: W.Workload, kv_lens=None):
+    x = W.make_inputs(w)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    kv = x.get("kv_lens") if kv_lens is None else kv_lens
+    kvd = None if kv is None else kv.to(DEV)
+    say(f"case {w.name} B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal} "
+        f"kv_lens={None if kv is None else kv.tolist()}")
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kvd)
+    torch.cuda.synchronize()
+    return x, q, k, v, kv, o, lse
+
+
+def _full_check(w, kv_lens=None):
+    x, q, k, v, kv, o, lse = _run(w, kv_lens)
+    o_ref, lse_ref = oracle_fwd(x["q"], x["k"], x["v"], w.scale, w.causal, kv)
+    if w.dtype == "f32":
+        check_o(to64(o), o_ref, F32_O)
+        check_lse(to64(lse), lse_ref, F32_LSE)
+    else:
+        check_o(to64(o), o_ref, BF16_O_MAX, BF16_O_MEAN)
+        check_lse(to64(lse), lse_ref, BF16_LSE_ABS, BF16_LSE_REL)
+    return x, o, lse
+
+
+# ---- the five workloads at their own sizes (workload 4 sampled) ----
+
+def test_workload1_fp32_full():
+    _full_check(W.BY_ID[1])
+
+
+def test_workload2_bf16_full():
+    _full_check(W.BY_ID[2])
+
+
+def test_workload3_causal_large_logits_full():
+    _full_check(W.BY_ID[3])
+
+
+def test_workload5_forward_full():
+    _full_check(W.BY_ID[5])
+
+
+def test_workload4_padded_sampled_rows():
+    w = W.BY_ID[4]
+    x, q, k, v, kv, o, lse = _run(w)
+    kvl = kv.tolist()
+    assert kvl[0] == 0 and kvl[1] == 1
+    # Closed-form rows on every head: kv_len 0 -> O = 0, lse = -inf; kv_len 1 -> O = V_0.
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.equal(o[1], v[1, :, :1, :].expand_as(o[1]))
+    s0 = (q[1].float() @ k[1, :, 0, :].float().unsqueeze(-1)).squeeze(-1) * w.scale
+    assert torch.max(torch.abs(lse[1] - s0)).item() < 1e-2
+    # Sampled rows against the oracle on two heads of every batch.
+    rng = np.random.default_rng(4)
+    N = w.N
+    o_h = to64(o)
+    lse_h = to64(lse)
+    for b in range(w.B):
+        L = kvl[b]
+        rows = {0, 1, 63, 64, 127, 128, N - 1, N - 64}
+        for r in (L - 2, L - 1, L, L + 1, L + 127):
+            if 0 <= r < N:
+                rows.add(r)
+        rows.update(int(r) for r in rng.integers(0, N, 24))
+        rows = sorted(rows)
+        heads = [(b, 0), (b, int(rng.integers(1, w.H)))]
+        o_ref, lse_ref = oracle_fwd(x["q"], x["k"], x["v"], w.scale, True, kv, rows=rows,
+                                    heads=heads)
+        for (bb, hh) in heads:
+            check_o(o_h[bb, hh, rows], o_ref[bb, hh], BF16_O_MAX)
+            check_lse(lse_h[bb, hh, rows], lse_ref[bb, hh], BF16_LSE_ABS, BF16_LSE_REL)
+
+
+# ---- edge cases at oracle-friendly sizes ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 77, 200, 333])
+def test_ragged_shapes(dtype, d, causal, N):
+    w = W.Workload(90, f"ragged N={N}", 2, 3, N, d, dtype, causal)
+    _full_check(w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_padding_with_empty_and_single_rows(dtype, causal):
+    w = W.Workload(91, "padding", 5, 2, 300, 64, dtype, causal)
+    kv = torch.tensor([0, 1, 150, 300, 64], dtype=torch.int32)
+    x, o, lse = _full_check(w, kv_lens=kv)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    v = x["v"].to(DEV)
+    assert torch.equal(o[1], v[1, :, :1, :].expand_as(o[1]))
+
+
+def test_kv_lens_out_of_range_are_clamped():
+    w = W.Workload(92, "clamp", 3, 1, 130, 64, "bf16", False)
+    x = W.make_inputs(w)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    o1, l1 = fa.fwd(q, k, v, kv_lens=torch.tensor([-5, 10**6, 130], dtype=torch.int32, device=DEV))
+    o2, l2 = fa.fwd(q, k, v, kv_lens=torch.tensor([0, 130, 130], dtype=torch.int32, device=DEV))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hidden_keys_never_leak(dtype):
+    """Cell D: overwriting hidden K/V rows with large finite values changes no bit."""
+    w = W.Workload(93, "leak", 2, 2, 256, 128, dtype, True)
+    x = W.make_inputs(w)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    kv = torch.tensor([200, 97], dtype=torch.int32, device=DEV)
+    o1, l1 = fa.fwd(q, k, v, causal=True, kv_lens=kv)
+    k2, v2 = k.clone(), v.clone()
+    k2[0, :, 200:] = 3000.0
+    v2[0, :, 200:] = -3000.0
+    k2[1, :, 97:] = -3000.0
+    v2[1, :, 97:] = 3000.0
+    o2, l2 = fa.fwd(q, k2, v2, causal=True, kv_lens=kv)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_causal_first_row_is_v0_and_deterministic():
+    w = W.BY_ID[5]
+    x = W.make_inputs(W.with_shape(w, N=1024))
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
+    for _ in range(3):
+        o2, lse2 = fa.fwd(q, k, v, causal=True)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def _embed(scores, values, d, dtype):
+    n = len(scores)
+    q = torch.zeros(1, 1, n, d, dtype=torch.float64)
+    q[0, 0, :, 0] = 1.0
+    k = torch.zeros_like(q)
+    k[0, 0, :, 0] = torch.tensor(scores, dtype=torch.float64)
+    v = torch.zeros_like(q)
+    vals = torch.tensor(values, dtype=torch.float64)
+    if vals.dim() == 1:
+        vals = vals[:, None]
+    v[0, 0, :, : vals.shape[1]] = vals
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def test_page_examples_through_fp32_kernel(golden):
+    """The pages' worked rows fed through fa_fwd_f32 (scale 1, one-hot embedding, d = 64)."""
+    for ex in golden["row_examples"]:
+        if any(isinstance(s, str) for s in ex["scores"]):
+            continue
+        say(f"page example {ex['id']}")
+        q, k, v = (t.to(DEV) for t in _embed(ex["scores"], ex["values"], 64, torch.float32))
+        n = len(ex["scores"])
+        o, lse = fa.fwd(q, k, v, scale=1.0)
+        # The last query row sees all keys in a non-causal call; every row has the same scores.
+        got = o[0, 0, n - 1, 0].item()
+        assert abs(got - ex["printed"]["O"]) <= ex["tol"]["O"] + 1e-5 * abs(got)
+    # Cell D through the causal mask, Cell D2 through an empty key range.
+    q, k, v = (t.to(DEV) for t in _embed([2.0, 1.0, 4.0, 3.0], [10.0, 20.0, 30.0, 40.0], 64,
+                                          torch.float32))
+    o, _ = fa.fwd(q, k, v, causal=True, scale=1.0)
+    want = (10 + 20 * math.exp(-1)) / (1 + math.exp(-1))
+    assert abs(o[0, 0, 1, 0].item() - want) < 1e-5
+    o, lse = fa.fwd(q, k, v, causal=True, scale=1.0,
+                    kv_lens=torch.zeros(1, dtype=torch.int32, device=DEV))
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    # Overflow example: scores 800 and 801 stay finite through the max shift.
+    q, k, v = (t.to(DEV) for t in _embed([800.0, 801.0], [10.0, 20.0], 64, torch.float32))
+    o, lse = fa.fwd(q, k, v, scale=1.0)
+    assert abs(o[0, 0, 1, 0].item() - 17.31058578630005) < 2e-5
+
+
+def test_fp32_matches_bf16_path_on_bf16_exact_inputs():
+    """Both paths compute the same attention; on bf16-exact inputs they agree to bf16 rounding."""
+    w = W.Workload(94, "cross", 2, 2, 512, 128, "bf16", True)
+    x = W.make_inputs(w)
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    o_b, l_b = fa.fwd(q, k, v, causal=True)
+    o_f, l_f = fa.fwd(q.float(), k.float(), v.float(), causal=True)
+    assert torch.max(torch.abs(o_b.float() - o_f)).item() < 2e-2
+    assert torch.max(torch.abs(l_b - l_f)).item() < 1e-3
