@@ -23,6 +23,11 @@ LIB = os.path.join(HERE, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
 
+# Per-source extra flags. The bf16 forward keeps its MFMA accumulators in
+# VGPRs (its rare rescale multiplies them with VALU instructions, which cannot
+# read AGPRs); Q operands are placed in AGPRs explicitly in the source.
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}",
@@ -46,7 +51,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + COMMON + EXTRA.get(src, []) + list(extra)
+           + ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

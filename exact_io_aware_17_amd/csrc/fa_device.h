@@ -13,6 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float POS_INF = __builtin_huge_valf();
@@ -66,6 +69,29 @@ __device__ __forceinline__ unsigned hi16(unsigned w) { return w >> 16; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4).
+// `lds` must be the same for the whole wave: lane l's 16 bytes land at
+// lds + 16 * l. Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): this wave's outstanding global loads (and LDS DMAs) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// (i % 4) of the 8-byte rows loaded by lanes 4j + i/4 (j = 0..3), i.e. four
+// lanes reading four consecutive rows hand every lane one column of them.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* lds) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lds);
+}
+
+// Sum of a packed pair of bf16 values added to an fp32 accumulator (v_dot2c_f32_bf16).
+__device__ __forceinline__ float add_bf16_pair(unsigned w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
 __device__ __forceinline__ void zero(f32x16& x) {

@@ -1,29 +1,44 @@
 // Exact attention forward for gfx950: bf16 matrix cores, fp32 online softmax.
 //
-// One workgroup owns BM = 32 * NW query rows of one (batch, head) and streams
-// the visible keys in blocks of BN = 64 through LDS, carrying per query row the
-// running max m, the running normaliser l and the unnormalised output (the
-// online recurrence of the interactive explainer "The Flash Attention";
-// "Exercises", the block merges). The score block and its probabilities live
-// only in registers.
+// One workgroup of NW = 4 waves owns BM = 128 query rows of one (batch, head)
+// and streams the visible keys in blocks of BN keys through LDS, carrying per
+// query row a reference max m, the running normaliser l and the unnormalised
+// output (the online recurrence of the interactive explainer "The Flash
+// Attention"; "Exercises", the block merges). The score block and its
+// probabilities live only in registers; only Q, K, V, O and lse touch device
+// memory.
 //
-// Layout choices (each wave owns 32 queries, one per lane pair):
+// Layout (each wave owns 32 queries, one per lane pair):
 //  * Scores are produced transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
-//    A = a 32-key x 16-dim slice of K (read from LDS), B = the wave's Q^T
-//    slice (held in registers for the whole kernel). In the 32x32 accumulator
-//    lane l holds query (l % 32) and 16 keys, so the row max and row sum are
-//    in-lane reductions plus one exchange between the two lane halves.
-//  * The output is accumulated transposed too, O^T += V^T P^T: B = P^T comes
-//    straight from the score registers (after bf16 rounding), A = V^T is read
-//    from a transposed copy of the V block in LDS whose key order is permuted
-//    (bits 2 and 3 of the key index swapped) so that it matches the order in
-//    which the accumulator registers hold the keys. The contraction index is
-//    free to permute, so no data moves between lanes.
-//  * The per-row rescale factor exp(m_old - m_new) is then a per-lane scalar.
-//  * Exponentials are base 2 with scale*log2(e) folded into one FMA.
-//  * K rows in LDS have their 16-byte chunks XOR-swizzled by row and the V^T
-//    rows by d, so the MFMA operand reads of 32 consecutive rows spread over
-//    all banks.
+//    A = a 32-key x 16-dim slice of K (LDS), B = the wave's Q^T slice (held in
+//    registers for the whole kernel). In the 32x32 accumulator lane l holds
+//    query (l % 32) and 16 keys, so row max and row sum are in-lane
+//    reductions plus one exchange between the two lane halves.
+//  * The output is accumulated transposed too, O^T += V^T P^T. B = P^T comes
+//    straight from the score registers after bf16 rounding; the contraction
+//    slots of the A operand are assigned to keys in the order the accumulator
+//    holds them (bits 2 and 3 of the key index swapped), which the contraction
+//    permits. A = V^T is read from the row-major V tile with the gfx950
+//    transpose read (ds_read_b64_tr_b16): four lanes reading four key rows
+//    give each lane four keys of one d column.
+//  * K and V tiles go from HBM to LDS with direct 16-byte loads (no register
+//    staging) through a ring of STAGES buffers: block j+STAGES-1 is in flight
+//    while block j is used. 16-byte chunks are XOR-swizzled per row so the
+//    operand reads hit every LDS bank evenly.
+//  * Registers are kept low enough for several waves per SIMD: their
+//    interleaving hides LDS and MFMA latency and overlaps one wave's softmax
+//    with another's matrix work.
+//  * The per-row rescale factor is a per-lane scalar. The reference max moves
+//    only when a block's max exceeds it by more than TAU (log2 units), so the
+//    accumulator rescale is skipped wave-wide in almost every block; any
+//    reference gives the same O = acc / l and lse = m + ln l exactly, and the
+//    lag bound keeps every exponential below 2^TAU.
+//  * Exponentials are base 2 (v_exp_f32) with scale*log2(e) folded into one
+//    FMA. Two row sums are kept: O is divided by the sum of the bf16-rounded
+//    weights that P V actually used (each output row is then a convex
+//    combination of V rows even where one weight dominates), and the
+//    logsumexp uses the sum of the fp32 probabilities (fp32 accuracy for the
+//    backward pass).
 //  * Causal: key blocks wholly in a wave's future are skipped ("Question
 //    bank": blocks entirely in the future are skipped); only blocks that
 //    straddle the diagonal or the padding length apply a mask.
@@ -39,29 +54,76 @@ namespace {
 
 using namespace dev;
 
-constexpr int BN = 64;  // keys per streamed block
+constexpr int NW = 4;         // waves per workgroup
+constexpr int BM = 32 * NW;   // queries per workgroup
+constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
 
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int KT_BYTES = BN * D * 2;   // K tile
-  constexpr int VT_BYTES = D * BN * 2;   // V^T tile
-  constexpr int STAGE = KT_BYTES + VT_BYTES;
-  constexpr int KCH = D / 8;             // 16-byte chunks per K row
-  constexpr int K_PER_T = BN * KCH / NT; // K chunks staged per thread
-  constexpr int V_PER_T = (BN / 2) * KCH / NT;  // (key pair, d chunk) units per thread
-  static_assert(K_PER_T >= 1 && V_PER_T >= 1, "tile too small for the workgroup");
+#ifndef FA_FWD_BN
+#define FA_FWD_BN 32
+#endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 2
+#endif
+#ifndef FA_FWD_WG_PER_CU
+#define FA_FWD_WG_PER_CU 3
+#endif
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+// K rows: 16-byte chunk c of row `row` is stored at slot c ^ kswz(row).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) {
+    return row & 15;
+  } else {
+    return (row >> 1) & 7;
+  }
+}
+
+// V rows: the transpose reads touch 8 consecutive rows x 4 chunks at a time.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) {
+    return 4 * (row & 3);
+  } else {
+    return 4 * ((row >> 1) & 1);
+  }
+}
+
+// s_waitcnt vmcnt(n) for n = 0 or n = K (K a compile-time count <= 15).
+template <int K>
+__device__ __forceinline__ void wait_vmem_upto(bool allow_k) {
+  static_assert(K <= 15, "vmcnt immediate must fit the low field");
+  if (allow_k) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | K);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+}
+
+template <int D, int BN, int STAGES, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int ROWB = D * 2;                 // bytes per K/V row
+  constexpr int TILE = BN * ROWB;             // bytes per K or V tile
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int DMA_PER_TILE = TILE / 1024;   // 1 KB (64 lanes x 16 B) per DMA instruction
+  constexpr int DPW = DMA_PER_TILE / NW;      // DMA instructions per wave per tile
+  constexpr int ROWS_PER_DMA = 1024 / ROWB;
+  constexpr int DC = D / 16;                  // 16-wide d chunks (S contraction)
+  constexpr int DT = D / 32;                  // 32-row d tiles of O^T
+  constexpr int KT = BN / 32;                 // 32-key MFMA tiles per block
+  constexpr int KC = BN / 16;                 // 16-key contraction chunks per block
+  static_assert(DMA_PER_TILE % NW == 0, "DMA blocks must split evenly over the waves");
+  static_assert(BN == 32 || BN == 64, "block of 32 or 64 keys");
+
+  __shared__ __attribute__((aligned(1024))) char kbuf[STAGES][TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf[STAGES][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = lane & 31;   // query within the wave / row within an MFMA tile
-  const int h = lane >> 5;   // lane half
+  const int n = lane & 31;  // query of this lane within the wave / row within an MFMA tile
+  const int h = lane >> 5;  // lane half
 
-  // ---- work assignment (a0: the tile schedule) ----
+  // ---- a0: tile schedule ----
   const int N = p.N;
   const int ntiles = (N + BM - 1) / BM;
   const int G = gridDim.x;
@@ -80,6 +142,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   int kend = kvlen;
   if (CAUSAL) kend = min(kend, q0 + BM);
   const int nblk = (kend + BN - 1) / BN;
+  const int qa = q0 + wave * 32;  // first query of this wave
+  const int qrow = qa + n;
 
   const size_t head = (size_t)bh * N * D;
   const __bf16* __restrict__ Q = (const __bf16*)p.q + head;
@@ -87,214 +151,199 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   const __bf16* __restrict__ V = (const __bf16*)p.v + head;
 
   // ---- Q^T fragments: lane (n, h) holds query qrow, dims 16c + 8h .. +8 ----
-  const int qa = q0 + wave * 32;  // first query of this wave
-  const int qrow = qa + n;
-  const int qrow_c = min(qrow, N - 1);
-  bf16x8 qf[D / 16];
+  bf16x8 qf[DC];
+  {
+    const int qrow_c = min(qrow, N - 1);
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qf[c] = *(const bf16x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
+    for (int c = 0; c < DC; ++c)
+      qf[c] = *(const bf16x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  f32x16 acc[D / 32];
+  // ---- a1: K/V block stream, HBM -> LDS ----
+  auto issue_block = [&](int j) {
+    if (j >= nblk) return;
+    const int key0 = j * BN;
+    char* ks = kbuf[j % STAGES];
+    char* vs = vbuf[j % STAGES];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+    for (int i = 0; i < DPW; ++i) {
+      const int blk = wave * DPW + i;
+      const int row = blk * ROWS_PER_DMA + lane / CPR;
+      const int pch = lane % CPR;
+      const size_t key = (size_t)min(key0 + row, N - 1);
+      dma16(K + key * D + (pch ^ kswz<D>(row)) * 8, ks + blk * 1024);
+      dma16(V + key * D + (pch ^ vswz<D>(row)) * 8, vs + blk * 1024);
+    }
+  };
+
+  // Per-lane LDS offsets of the operand reads (the block-independent parts).
+  int koff[DC];  // K row n (+32 per key tile), logical chunk 2c + h
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  float m_run = NEG_INF;  // running max, in units of scale*log2(e)*score
-  float l_run = 0.f;      // this lane's share of the running normaliser
+  for (int c = 0; c < DC; ++c) koff[c] = n * ROWB + (((2 * c + h) ^ kswz<D>(n)) * 16);
+  // V^T transpose reads: row 16*kc + 8r + 4h + (lane%16)/4, column
+  // dt*32 + 16*((lane/16)%2) + 4*(lane%4) (four bf16 = 8 bytes). The swizzle
+  // depends only on the row's low bits, which 16*kc + 8r leaves unchanged.
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vrow = 4 * h + ((lane & 15) >> 2);
+  int voff[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int col = dt * 32 + vcol;
+    voff[dt] = vrow * ROWB + (((col >> 3) ^ vswz<D>(vrow)) * 16) + (col & 7) * 2;
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
+  float m_run = NEG_INF;  // reference max (scaled log2 units)
+  float l_run = 0.f;      // this lane's share of sum p (fp32)
+  float l_bf = 0.f;       // the same over the bf16-rounded p used by P V
   const float scl = p.scale_log2;
 
-  // ---- staging registers for the next K/V block ----
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T][2];
-
-  auto load_block = [&](int j) {
-    const int key0 = j * BN;
+  // Prologue: blocks 0 .. STAGES-2 in flight.
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int u = tid + NT * i;
-      const int row = u / KCH, c = u % KCH;
-      const int key = min(key0 + row, N - 1);
-      kreg[i] = *(const u32x4*)(K + (size_t)key * D + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + NT * i;
-      const int dc = u % KCH, kp = u / KCH;
-      const int k0 = min(key0 + 2 * kp, N - 1);
-      const int k1 = min(key0 + 2 * kp + 1, N - 1);
-      vreg[i][0] = *(const u32x4*)(V + (size_t)k0 * D + dc * 8);
-      vreg[i][1] = *(const u32x4*)(V + (size_t)k1 * D + dc * 8);
-    }
-  };
-  auto store_block = [&](int buf) {
-    char* ks = smem + buf * STAGE;
-    char* vs = ks + KT_BYTES;
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int u = tid + NT * i;
-      const int row = u / KCH, c = u % KCH;
-      *(u32x4*)(ks + row * (D * 2) + row_slot<D>(row, c) * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + NT * i;
-      const int dc = u % KCH, kp = u / KCH;
-      const int pos = swap23(2 * kp);  // even; the odd key of the pair sits at pos + 1
-      const unsigned* w0 = (const unsigned*)&vreg[i][0];
-      const unsigned* w1 = (const unsigned*)&vreg[i][1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc * 8 + e;
-        const unsigned lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-        const unsigned hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
-        *(unsigned*)(vs + d * (BN * 2) + t64_slot(d, pos >> 3) * 16 + (pos & 7) * 2) =
-            lo | (hi << 16);
-      }
-    }
-  };
-
-  if (nblk > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
+  for (int j = 0; j < STAGES - 1; ++j) issue_block(j);
+  __builtin_amdgcn_sched_barrier(0);
 
   for (int j = 0; j < nblk; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nblk) load_block(j + 1);
+    // Block j has landed once at most the DMAs of the blocks issued after it
+    // (j+1 .. j+STAGES-2) are outstanding; this wave's only vector-memory
+    // instructions from here on are these DMAs.
+    if constexpr (STAGES == 2) {
+      wait_vmem_upto<0>(false);
+    } else {
+      static_assert(STAGES == 3, "ring of 2 or 3 stages");
+      wait_vmem_upto<2 * DPW>(j + 1 < nblk);
+    }
+    __syncthreads();               // all waves: block j landed, block j-1's stage is free
+    issue_block(j + STAGES - 1);   // into the stage block j-1 used
 
     const int key0 = j * BN;
     // Skip blocks wholly in this wave's future (all its rows would be masked).
-    const bool wave_skip = CAUSAL && (key0 > qa + 31);
-    if (!wave_skip) {
-      const char* ks = smem + buf * STAGE;
-      const char* vs = ks + KT_BYTES;
+    if (CAUSAL && key0 > qa + 31) continue;
+    const char* ks = kbuf[j % STAGES];
+    const char* vs = vbuf[j % STAGES];
 
-      // ---- a2: S^T = K Q^T for 64 keys x 32 queries ----
-      f32x16 s[2];
+    // ---- a2: S^T = K Q^T for BN keys x 32 queries ----
+    f32x16 s[KT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < KT; ++t) zero(s[t]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
+    for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row = t * 32 + n;
-          const bf16x8 a = *(const bf16x8*)(ks + row * (D * 2) + row_slot<D>(row, 2 * c + h) * 16);
-          s[t] = mfma32(a, qf[c], s[t]);
-        }
-      }
+      for (int t = 0; t < KT; ++t)
+        s[t] = mfma32(*(const bf16x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
 
-      // ---- a3: mask (only on blocks that straddle the diagonal or kv_len) ----
-      const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa);
-      if (need_mask) {
+    // ---- a3: mask (only blocks that straddle the diagonal or kv_len) ----
+    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa);
+    if (need_mask) {
+      int lim = kvlen - 1;  // key visible iff key <= lim
+      if (CAUSAL) lim = min(lim, qrow);
+      lim -= key0 + 4 * h;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool hide = (key >= kvlen) || (CAUSAL && key > qrow);
-            if (hide) s[t][r] = NEG_INF;
-          }
-      }
-
-      // ---- a4: online softmax ----
-      float mx = NEG_INF;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * scl);
-      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;  // all hidden so far: keep p = 0
-      const float corr = exp2f(m_run - m_use);               // 0 when m_run = -inf
-      float rs = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = exp2f(fmaf(s[t][r], scl, -m_use));
-          s[t][r] = pv;
-          rs += pv;
-        }
-      l_run = l_run * corr + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[t][r] *= corr;
-
-      // ---- P^T fragments (bf16): chunk kc = registers 8*(kc%2).. of tile kc/2 ----
-      bf16x8 pf[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack_bf16x2(s[kc >> 1][8 * (kc & 1) + 2 * e], s[kc >> 1][8 * (kc & 1) + 2 * e + 1]);
-        pf[kc] = __builtin_bit_cast(bf16x8, w);
-      }
-
-      // ---- a5: O^T += V^T P^T ----
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        const int drow = t * 32 + n;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16x8 a = *(const bf16x8*)(vs + drow * (BN * 2) + t64_slot(drow, 2 * kc + h) * 16);
-          acc[t] = mfma32(a, pf[kc], acc[t]);
-        }
-      }
+        for (int r = 0; r < 16; ++r)
+          if (t * 32 + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = NEG_INF;
     }
 
-    if (j + 1 < nblk) store_block(buf ^ 1);
-    __syncthreads();
+    // ---- a4: online softmax ----
+    float mx = NEG_INF;
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    const float mt = pair_max(mx) * scl;  // block max, scaled (-inf if all hidden)
+    const bool up = mt > m_run + TAU;
+    if (__any(up)) {
+      const float m_new = up ? mt : m_run;
+      const float corr = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
+      l_run *= corr;
+      l_bf *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == NEG_INF) ? 0.f : m_run;  // nothing visible yet: p = 0
+
+    // P^T fragments (bf16): chunk kc = registers 8*(kc%2) .. +8 of tile kc/2.
+    bf16x8 pf[KC];
+    float rs = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * (kc & 1) + 2 * e;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], scl, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r + 1], scl, -m_use));
+        w[e] = pack_bf16x2(p0, p1);
+        rs += p0 + p1;
+        l_bf = add_bf16_pair(w[e], l_bf);
+      }
+      pf[kc] = __builtin_bit_cast(bf16x8, w);
+    }
+    l_run += rs;
+
+    // ---- a5: O^T += V^T P^T ----
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const i16x4 lo = lds_read_tr16(vs + kc * 16 * ROWB + voff[dt]);
+        const i16x4 hi = lds_read_tr16(vs + (kc * 16 + 8) * ROWB + voff[dt]);
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = mfma32(a, pf[kc], acc[dt]);
+      }
   }
+  wait_vmem();  // no DMA may still target this workgroup's LDS at exit
 
   // ---- a6: finalize ----
   const float l_tot = pair_sum(l_run);
+  const float l_o = pair_sum(l_bf);
   const bool empty = (l_tot == 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
+  const float inv = empty ? 0.f : 1.f / l_o;
   if (qrow < N) {
     __bf16* O = (__bf16*)p.o + head + (size_t)qrow * D;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack_bf16x2(acc[t][4 * g] * inv, acc[t][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(acc[t][4 * g + 2] * inv, acc[t][4 * g + 3] * inv);
-        *(u32x2*)(O + t * 32 + 8 * g + 4 * h) = w;
+        w[0] = pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        *(u32x2*)(O + dt * 32 + 8 * g + 4 * h) = w;
       }
     if (h == 0 && p.lse) {
-      p.lse[(size_t)bh * N + qrow] =
-          empty ? NEG_INF : (m_run + log2f(l_tot)) * LN2;
+      p.lse[(size_t)bh * N + qrow] = empty ? NEG_INF : (m_run + log2f(l_tot)) * LN2;
     }
   }
 }
 
-template <int D, int NW>
+template <int D>
 hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int BM = 32 * NW;
+  constexpr int BN = FA_FWD_BN, ST = FA_FWD_STAGES;
   const long long ntiles = (p.N + BM - 1) / BM;
   const long long grid = (long long)p.B * p.H * ntiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, false>), dim3((unsigned)grid), dim3(NW * 64),
+                       0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 128) return launch_d<128, 4>(p, stream);
-  if (p.d == 64) return launch_d<64, 4>(p, stream);
+  if (p.d == 128) return launch_d<128>(p, stream);
+  if (p.d == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 
