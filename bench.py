@@ -93,6 +93,68 @@ def cpu_baseline(x, w, budget_s: float = 12.0):
     }
 
 
+COPY_BYTES = 256 * 2 ** 20  # calibration copy: 256 MiB read + 256 MiB written
+
+
+def profile_run(w) -> int:
+    """A short run for counter collection: a plain copy of known size, then the
+    forward kernel, three times each."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    from exact_io_aware_17_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    x = W.make_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kv = x["kv_lens"].to(dev) if "kv_lens" in x else None
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kv)
+    torch.cuda.synchronize()
+    print("profile run done", flush=True)
+    return 0
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
+    """HBM bytes per fa_fwd launch from FETCH_SIZE / WRITE_SIZE counter runs of
+    --profile-run, each scaled by what the counter reads for the known copy."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    out = {"kernel_source_hash": kernel_source_hash(), "command": command,
+           "copy_bytes": COPY_BYTES}
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        rows = read(d, counter)
+        copy = [v for n, v in rows if "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
+        fwd = [v for n, v in rows if "fwd_bf16" in n]
+        if not copy or not fwd:
+            print(f"no {counter} readings for the copy or the forward kernel", file=sys.stderr)
+            return 1
+        scale = COPY_BYTES / (sorted(copy)[len(copy) // 2] * 1024.0)
+        per_launch = sorted(fwd)[len(fwd) // 2] * 1024.0 * scale
+        out[key + "_kib_raw"] = sorted(fwd)[len(fwd) // 2]
+        out[key + "_scale"] = scale
+        out[key + "_bytes_per_launch"] = per_launch
+    out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +163,16 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="short run (copy calibration + forward) for rocprofv3 counters")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn FETCH_SIZE / WRITE_SIZE runs of --profile-run into "
+                         "the committed traffic summary")
+    ap.add_argument("--traffic-command", default="",
+                    help="the profiling command recorded in the traffic summary")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, args.traffic_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -113,6 +184,8 @@ def main() -> int:
     from exact_io_aware_17_amd import workloads as W
 
     w = W.BY_ID[args.workload]
+    if args.profile_run:
+        return profile_run(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = W.make_inputs(W.with_shape(w, backward=True))
@@ -178,7 +251,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128,4,causal>",
+            "kernel": "fwd_bf16_kernel<128,32,2,causal>",
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_kernel, 5),
             "kernel_ms_min": round(per_launch[0], 5),
