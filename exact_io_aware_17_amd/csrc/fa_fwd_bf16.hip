@@ -64,6 +64,9 @@ constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 2
 #endif
+#ifndef FA_PRIO_MFMA
+#define FA_PRIO_MFMA 1  // wave priority (s_setprio) during the MFMA phases
+#endif
 #ifndef FA_FWD_WG_PER_CU
 #define FA_FWD_WG_PER_CU 3
 #endif
@@ -226,6 +229,10 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     const char* vs = vbuf[j % STAGES];
 
     // ---- a2: S^T = K Q^T for BN keys x 32 queries ----
+    // Waves in a matrix phase get issue priority over waves in their softmax,
+    // so whichever wave has MFMAs ready keeps the matrix pipe fed while the
+    // others' VALU work fills the gaps.
+    __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
     f32x16 s[KT];
 #pragma unroll
     for (int t = 0; t < KT; ++t) zero(s[t]);
@@ -235,6 +242,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
       for (int t = 0; t < KT; ++t)
         s[t] = mfma32(*(const bf16x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- a3: mask (only blocks that straddle the diagonal or kv_len) ----
     const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa);
     if (need_mask) {
@@ -288,6 +296,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     }
     l_run += rs;
 
+    __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
     // ---- a5: O^T += V^T P^T ----
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -300,6 +309,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
         acc[dt] = mfma32(a, pf[kc], acc[dt]);
       }
   }
+  __builtin_amdgcn_s_setprio(0);
   wait_vmem();  // no DMA may still target this workgroup's LDS at exit
 
   // ---- a6: finalize ----
