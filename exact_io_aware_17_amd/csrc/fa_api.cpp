@@ -142,6 +142,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.dk = dk;
   p.dv = dv;
   p.delta = (float*)workspace;
+  p.lse2 = (float*)((char*)workspace + wbytes / 2);
   p.kv_lens = kv_lens;
   p.B = B;
   p.H = H;

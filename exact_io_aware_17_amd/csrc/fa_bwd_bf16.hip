@@ -7,17 +7,22 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
 //   dK = scale dS^T Q.
 // Three kernels, no atomics:
-//   delta  D_i for every row (fp32, into the caller's workspace);
-//   dq     one workgroup per 32*NW query rows streams the visible key blocks:
+//   prep   D_i and lse_i*log2(e) (+inf for an empty row, so that P = 0) for
+//          every row, into the caller's workspace;
+//   dq     one workgroup per 128 query rows streams the visible key blocks:
 //          S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (the forward's
 //          transposed layout: one query per lane pair);
-//   dkdv   one workgroup per 32*NW keys streams the query blocks that see
+//   dkdv   one workgroup per 128 keys streams the query blocks that see
 //          them: S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
 //          (one key per lane pair).
-// Operands that feed an MFMA contraction over the streamed index are staged
-// in LDS twice: row-major (16-byte chunks XOR-swizzled by row) and
-// transposed with the streamed index permuted by swap23, matching the order
-// in which a 32x32 accumulator holds its rows.
+// Streamed blocks go from HBM to LDS with direct 16-byte loads into a double
+// buffer, stored once, row-major. The same copy is read two ways: as rows
+// (ds_read_b128, the A operand of the S / dP products) and transposed
+// (ds_read_b64_tr_b16, the A operand of the products that contract over the
+// streamed rows). The 16-byte chunks of a row are XOR-swizzled with a pattern
+// that keeps both kinds of read free of bank conflicts. Contraction slots over
+// the streamed rows follow the order in which a 32x32 accumulator holds its
+// rows (bits 2 and 3 swapped), as in the forward kernel.
 #include "fa_internal.h"
 #include "fa_device.h"
 
@@ -28,14 +33,43 @@ namespace {
 
 using namespace dev;
 
-constexpr int BS = 64;  // streamed rows (keys in dq, queries in dkdv) per block
+constexpr int BS = 32;   // streamed rows per block (keys in dq, queries in dkdv)
+constexpr int NWB = 4;   // waves per workgroup
+constexpr int BT = 32 * NWB;  // rows owned by a workgroup (queries in dq, keys in dkdv)
+
+// Waves per SIMD each kernel's register budget is sized for.
+#ifndef FA_BWD_DQ_OCC
+#define FA_BWD_DQ_OCC 2
+#endif
+#ifndef FA_BWD_DKDV128_OCC
+#define FA_BWD_DKDV128_OCC 2
+#endif
+
+// 16-byte chunk c of row `row` of a streamed tile is stored at c ^ tswz(row):
+// 16 consecutive rows read at one chunk, and 8 consecutive rows read 4 chunks
+// each by the transpose reads, both spread evenly over the LDS banks.
+template <int D>
+__device__ __forceinline__ int tswz(int row) {
+  if constexpr (D == 128) {
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  } else {
+    return ((row >> 1) & 1) | (((row >> 2) & 1) << 2) | (((row >> 3) & 1) << 1);
+  }
+}
 
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// ---- a7: D_i = sum_c dO_ic O_ic ----
+// Tile-major work order: workgroup id w takes tile rank w / (B*H) of head
+// w % (B*H). Workgroups are dispatched in id order, round-robin over the 8
+// XCDs, so each XCD starts with the heaviest tiles and, when B*H is a multiple
+// of 8, keeps to a fixed set of heads (shared L2).
+__device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
+__device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
+
+// ---- a7 (and the lse preparation): per row D_i and lse_i * log2(e) ----
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const long long rows = (long long)p.B * p.H * p.N;
@@ -53,52 +87,73 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) p.delta[row] = acc;
-}
-
-// Stage rows [r0, r0 + BS) of a row-major [N, D] bf16 matrix into LDS, as a
-// row-major copy (`rm`, may be null) and a transposed copy (`tr`, may be
-// null) whose row index is permuted by swap23. Rows past N repeat row N-1.
-template <int D, int NT>
-__device__ __forceinline__ void stage_rows(const __bf16* __restrict__ X, int r0, int N, char* rm,
-                                           char* tr, int tid) {
-  constexpr int KCH = D / 8;
-  constexpr int UNITS = (BS / 2) * KCH;
-  static_assert(UNITS % NT == 0, "staging units must divide evenly");
-#pragma unroll
-  for (int i = 0; i < UNITS / NT; ++i) {
-    const int u = tid + NT * i;
-    const int dc = u % KCH, rp = u / KCH;
-    const int ra = min(r0 + 2 * rp, N - 1);
-    const int rb = min(r0 + 2 * rp + 1, N - 1);
-    const u32x4 xa = *(const u32x4*)(X + (size_t)ra * D + dc * 8);
-    const u32x4 xb = *(const u32x4*)(X + (size_t)rb * D + dc * 8);
-    if (rm) {
-      *(u32x4*)(rm + (2 * rp) * (D * 2) + row_slot<D>(2 * rp, dc) * 16) = xa;
-      *(u32x4*)(rm + (2 * rp + 1) * (D * 2) + row_slot<D>(2 * rp + 1, dc) * 16) = xb;
-    }
-    if (tr) {
-      const int pos = swap23(2 * rp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc * 8 + e;
-        const unsigned lo = (e & 1) ? hi16(xa[e >> 1]) : lo16(xa[e >> 1]);
-        const unsigned hi = (e & 1) ? hi16(xb[e >> 1]) : lo16(xb[e >> 1]);
-        *(unsigned*)(tr + d * (BS * 2) + t64_slot(d, pos >> 3) * 16 + (pos & 7) * 2) =
-            lo | (hi << 16);
-      }
-    }
+  if (row < rows && c == 0) {
+    p.delta[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = (l == NEG_INF) ? POS_INF : l * LOG2E;  // empty row: P = 0
   }
 }
 
-// Work id with the XCD-contiguous remap (workgroups go round-robin over 8 XCDs).
-__device__ __forceinline__ int work_id() {
-  const int G = gridDim.x, bid = blockIdx.x;
-  return (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+// DMA of rows [r0, r0 + BS) of a row-major [N, D] bf16 matrix into an LDS tile
+// (rows past N repeat row N-1; they are masked by the callers).
+template <int D>
+__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ X, int r0, int N, char* dst,
+                                           int wave, int lane) {
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = ROWB / 16;
+  constexpr int DMA_PER_TILE = BS * ROWB / 1024;
+  constexpr int DPW = DMA_PER_TILE / NWB;
+  constexpr int ROWS_PER_DMA = 1024 / ROWB;
+  static_assert(DMA_PER_TILE % NWB == 0, "tile DMAs split evenly over the waves");
+#pragma unroll
+  for (int e = 0; e < DPW; ++e) {
+    const int blk = wave * DPW + e;
+    const int row = blk * ROWS_PER_DMA + lane / CPR;
+    const int pch = lane % CPR;
+    const size_t src = (size_t)min(r0 + row, N - 1);
+    dma16(X + src * D + (pch ^ tswz<D>(row)) * 8, dst + blk * 1024);
+  }
 }
 
-// Store a transposed 32x32-tiled accumulator (lane = one row of the output,
-// registers = D columns in groups of 4) as bf16, times `mul`.
+// Per-lane offsets of the two kinds of operand read of a streamed tile.
+//  row read:  A operand rows n (of 32), logical chunk 2c + h     -> roff[c]
+//  tr read:   A operand d rows dt*32 + (lane%32), slots over the streamed rows
+//             16*kc + 8*r + 4*h + (lane%16)/4                     -> toff[dt][r]
+//             (+ kc*16 rows, an immediate offset)
+template <int D>
+struct TileOffsets {
+  int roff[D / 16];
+  int toff[D / 32][2];
+  __device__ __forceinline__ TileOffsets(int lane) {
+    constexpr int ROWB = D * 2;
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) roff[c] = n * ROWB + (((2 * c + h) ^ tswz<D>(n)) * 16);
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int vrow = 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = 8 * r + vrow;
+        const int col = dt * 32 + vcol;
+        toff[dt][r] = row * ROWB + (((col >> 3) ^ tswz<D>(row)) * 16) + (col & 7) * 2;
+      }
+  }
+};
+
+// Transposed A operand (d rows dt*32.., streamed-row chunk kc) of a tile.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, const TileOffsets<D>& o, int dt,
+                                             int kc) {
+  constexpr int ROWB = D * 2;
+  const i16x4 lo = lds_read_tr16(tile + kc * 16 * ROWB + o.toff[dt][0]);
+  const i16x4 hi = lds_read_tr16(tile + kc * 16 * ROWB + o.toff[dt][1]);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Store a transposed accumulator (lane = one output row, registers = D
+// columns in groups of 4) as bf16, times `mul`.
 template <int D>
 __device__ __forceinline__ void store_rowT(__bf16* dst, const f32x16* acc, float mul, int h) {
 #pragma unroll
@@ -112,31 +167,27 @@ __device__ __forceinline__ void store_rowT(__bf16* dst, const f32x16* acc, float
     }
 }
 
-// ---- dQ: one workgroup per 32*NW query rows ----
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int BM = 32 * NW;
-  constexpr int NT = NW * 64;
+// ---- dQ: one workgroup per 128 query rows ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdParams p) {
   constexpr int TB = BS * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[3 * TB];
-  char* ks = smem;           // K block, row-major
-  char* vs = smem + TB;      // V block, row-major
-  char* kts = smem + 2 * TB; // K block, transposed (keys permuted)
+  constexpr int DC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char kbuf[2][TB];  // K block, row-major
+  __shared__ __attribute__((aligned(1024))) char vbuf[2][TB];  // V block, row-major
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N;
-  const int ntiles = (N + BM - 1) / BM;
-  const int lid = work_id();
-  const int bh = lid / ntiles;
-  int tile = lid % ntiles;
-  if (CAUSAL) tile = ntiles - 1 - tile;
+  const int ntiles = (N + BT - 1) / BT;
+  const int bh = tile_head(p.B * p.H);
+  int tile = tile_rank(p.B * p.H);
+  if (CAUSAL) tile = ntiles - 1 - tile;  // the latest query rows see the most keys
   const int b = bh / p.H;
-  const int q0 = tile * BM;
+  const int q0 = tile * BT;
   int kvlen = N;
   if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
   int kend = kvlen;
-  if (CAUSAL) kend = min(kend, q0 + BM);
+  if (CAUSAL) kend = min(kend, q0 + BT);
   const int nblk = (kend + BS - 1) / BS;
 
   const size_t head = (size_t)bh * N * D;
@@ -148,102 +199,97 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p) {
   const int qa = q0 + wave * 32;
   const int qrow = qa + n;
   const int qrow_c = min(qrow, N - 1);
-  bf16x8 qf[D / 16], of[D / 16];
+  bf16x8 qf[DC], of[DC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < DC; ++c) {
     qf[c] = *(const bf16x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
     of[c] = *(const bf16x8*)(dO + (size_t)qrow_c * D + 16 * c + 8 * h);
   }
-  const float lse = p.lse[(size_t)bh * N + qrow_c];
-  const float lse2 = (lse == NEG_INF) ? POS_INF : lse * LOG2E;  // empty row: P = 0
+  const float lse2 = p.lse2[(size_t)bh * N + qrow_c];
   const float dl = p.delta[(size_t)bh * N + qrow_c];
+  __builtin_amdgcn_sched_barrier(0);
   const float scl = p.scale_log2;
+  const TileOffsets<D> off(lane);
 
-  f32x16 acc[D / 32];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) zero(acc[t]);
+  for (int t = 0; t < DT; ++t) zero(acc[t]);
 
+  auto issue = [&](int j) {
+    if (j >= nblk) return;
+    issue_tile<D>(K, j * BS, N, kbuf[j & 1], wave, lane);
+    issue_tile<D>(V, j * BS, N, vbuf[j & 1], wave, lane);
+  };
+  issue(0);
   for (int j = 0; j < nblk; ++j) {
+    wait_vmem();
+    __syncthreads();
+    issue(j + 1);
     const int key0 = j * BS;
-    __syncthreads();
-    stage_rows<D, NT>(K, key0, N, ks, kts, tid);
-    stage_rows<D, NT>(V, key0, N, vs, nullptr, tid);
-    __syncthreads();
     if (CAUSAL && key0 > qa + 31) continue;  // wholly in this wave's future
+    const char* ks = kbuf[j & 1];
+    const char* vs = vbuf[j & 1];
 
-    f32x16 s[2], dp[2];
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s, dp;
+    zero(s);
+    zero(dp);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      zero(s[t]);
-      zero(dp[t]);
+    for (int c = 0; c < DC; ++c) {
+      s = mfma32(*(const bf16x8*)(ks + off.roff[c]), qf[c], s);
+      dp = mfma32(*(const bf16x8*)(vs + off.roff[c]), of[c], dp);
     }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = t * 32 + n;
-        const int off = row * (D * 2) + row_slot<D>(row, 2 * c + h) * 16;
-        s[t] = mfma32(*(const bf16x8*)(ks + off), qf[c], s[t]);
-        dp[t] = mfma32(*(const bf16x8*)(vs + off), of[c], dp[t]);
-      }
+    __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa);
+    int lim = kvlen - 1;  // key visible iff key <= lim
+    if (CAUSAL) lim = min(lim, qrow);
+    lim -= key0 + 4 * h;
+    bf16x8 df[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2f(fmaf(s[t][r], scl, -lse2));
-        if (need_mask) {
-          const int key = key0 + t * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= kvlen || (CAUSAL && key > qrow)) pv = 0.f;
-        }
-        s[t][r] = pv * (dp[t][r] - dl);  // dS^T
-      }
-    bf16x8 df[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < 2; ++kc) {
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack_bf16x2(s[kc >> 1][8 * (kc & 1) + 2 * e], s[kc >> 1][8 * (kc & 1) + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r = 8 * kc + 2 * e + u;
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -lse2));
+          if (need_mask && 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
+          v2[u] = pv * (dp[r] - dl);  // dS^T
+        }
+        w[e] = pack_bf16x2(v2[0], v2[1]);
+      }
       df[kc] = __builtin_bit_cast(bf16x8, w);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      const int drow = t * 32 + n;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 a = *(const bf16x8*)(kts + drow * (BS * 2) + t64_slot(drow, 2 * kc + h) * 16);
-        acc[t] = mfma32(a, df[kc], acc[t]);
-      }
-    }
+      for (int kc = 0; kc < 2; ++kc) acc[dt] = mfma32(tr_operand<D>(ks, off, dt, kc), df[kc], acc[dt]);
+    __builtin_amdgcn_s_setprio(0);
   }
+  wait_vmem();
 
   if (qrow < N) store_rowT<D>((__bf16*)p.dq + head + (size_t)qrow * D, acc, p.scale, h);
 }
 
-// ---- dK, dV: one workgroup per 32*NW keys ----
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BK = 32 * NW;
-  constexpr int NT = NW * 64;
+// ---- dK, dV: one workgroup per 128 keys ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int TB = BS * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB];
-  __shared__ __attribute__((aligned(16))) float lse2s[BS];
-  __shared__ __attribute__((aligned(16))) float dls[BS];
-  char* qs = smem;            // Q block, row-major
-  char* os = smem + TB;       // dO block, row-major
-  char* qts = smem + 2 * TB;  // Q block, transposed (queries permuted)
-  char* ots = smem + 3 * TB;  // dO block, transposed (queries permuted)
+  constexpr int DC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char qbuf[2][TB];  // Q block, row-major
+  __shared__ __attribute__((aligned(1024))) char obuf[2][TB];  // dO block, row-major
+  __shared__ __attribute__((aligned(16))) float stat[2][64];   // lse*log2(e), then D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N;
-  const int ntiles = (N + BK - 1) / BK;
-  const int lid = work_id();
-  const int bh = lid / ntiles;
-  const int tile = lid % ntiles;  // low key tiles see the most queries: they go first
+  const int bh = tile_head(p.B * p.H);
+  const int tile = tile_rank(p.B * p.H);  // the earliest keys are seen by the most queries
   const int b = bh / p.H;
-  const int kb0 = tile * BK;
+  const int kb0 = tile * BT;
   int kvlen = N;
   if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
 
@@ -252,102 +298,120 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p) {
   const __bf16* K = (const __bf16*)p.k + head;
   const __bf16* V = (const __bf16*)p.v + head;
   const __bf16* dO = (const __bf16*)p.dout + head;
-  const float* lse = p.lse + (size_t)bh * N;
-  const float* delta = p.delta + (size_t)bh * N;
+  const float* lse2g = p.lse2 + (size_t)bh * N;
+  const float* deltag = p.delta + (size_t)bh * N;
 
   const int kw0 = kb0 + wave * 32;
   const int key = kw0 + n;
   const int key_c = min(key, N - 1);
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[DC], vf[DC];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < DC; ++c) {
     kf[c] = *(const bf16x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
     vf[c] = *(const bf16x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
   }
+  __builtin_amdgcn_sched_barrier(0);
   const float scl = p.scale_log2;
+  const TileOffsets<D> off(lane);
 
-  f32x16 dva[D / 32], dka[D / 32];
+  f32x16 dva[DT], dka[DT];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
+  for (int t = 0; t < DT; ++t) {
     zero(dva[t]);
     zero(dka[t]);
   }
 
   const int nqb = (N + BS - 1) / BS;
   const int qstart = CAUSAL ? kb0 / BS : 0;
-  const bool active = kb0 < kvlen;  // otherwise every key of the tile is hidden
-  for (int ib = active ? qstart : nqb; ib < nqb; ++ib) {
-    const int qb0 = ib * BS;
-    __syncthreads();
-    stage_rows<D, NT>(Q, qb0, N, qs, qts, tid);
-    stage_rows<D, NT>(dO, qb0, N, os, ots, tid);
-    if (tid < BS) {
-      const int qi = min(qb0 + tid, N - 1);
-      const float l = lse[qi];
-      lse2s[tid] = (l == NEG_INF) ? POS_INF : l * LOG2E;
-      dls[tid] = delta[qi];
+  const int qend = (kb0 < kvlen) ? nqb : qstart;  // every key of the tile hidden: nothing to do
+  auto issue = [&](int i) {
+    if (i >= qend) return;
+    issue_tile<D>(Q, i * BS, N, qbuf[i & 1], wave, lane);
+    issue_tile<D>(dO, i * BS, N, obuf[i & 1], wave, lane);
+    if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
+      const int qi = min(i * BS + (lane & 31), N - 1);
+      const float* src = (lane < 32) ? lse2g + qi : deltag + qi;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)stat[i & 1], 4, 0, 0);
     }
+  };
+  issue(qstart);
+  for (int i = qstart; i < qend; ++i) {
+    wait_vmem();
     __syncthreads();
-    if (kw0 >= kvlen) continue;                    // all of this wave's keys are hidden
-    if (CAUSAL && kw0 > qb0 + BS - 1) continue;    // every query of the block precedes them
+    issue(i + 1);
+    const int qb0 = i * BS;
+    if (kw0 >= kvlen) continue;                  // all of this wave's keys are hidden
+    if (CAUSAL && kw0 > qb0 + BS - 1) continue;  // every query of the block precedes them
+    const char* qs = qbuf[i & 1];
+    const char* os = obuf[i & 1];
+    const float* st = stat[i & 1];
 
-    const bool need_mask =
-        (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0);
-    f32x16 pt[2], dst[2];
+    // Phases in order, each value dead as soon as it is consumed: S, P, dV^T
+    // (needs P), dP, dS (needs P and dP), dK^T.
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s;
+    zero(s);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      f32x16 s, dp;
-      zero(s);
-      zero(dp);
+    for (int c = 0; c < DC; ++c) s = mfma32(*(const bf16x8*)(qs + off.roff[c]), kf[c], s);
+    __builtin_amdgcn_s_setprio(0);
+    const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0);
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const int row = qt * 32 + n;
-        const int off = row * (D * 2) + row_slot<D>(row, 2 * c + h) * 16;
-        s = mfma32(*(const bf16x8*)(qs + off), kf[c], s);
-        dp = mfma32(*(const bf16x8*)(os + off), vf[c], dp);
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ql = qt * 32 + 8 * g + 4 * h;  // four consecutive queries
-        const f32x4 l4 = *(const f32x4*)(lse2s + ql);
-        const f32x4 d4 = *(const f32x4*)(dls + ql);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pv = exp2f(fmaf(s[r], scl, -l4[e]));
-          if (need_mask) {
-            const int query = qb0 + ql + e;
-            if (key >= kvlen || query >= N || (CAUSAL && key > query)) pv = 0.f;
-          }
-          pt[qt][r] = pv;
-          dst[qt][r] = pv * (dp[r] - d4[e]);
-        }
-      }
-    }
-    bf16x8 pf[4], df[4];
-#pragma unroll
-    for (int qc = 0; qc < 4; ++qc) {
-      u32x4 wp, wd;
+    for (int g = 0; g < 4; ++g) {
+      const int ql = 8 * g + 4 * h;  // four consecutive queries of this lane
+      const f32x4 l4 = *(const f32x4*)(st + ql);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 8 * (qc & 1) + 2 * e;
-        wp[e] = pack_bf16x2(pt[qc >> 1][r], pt[qc >> 1][r + 1]);
-        wd[e] = pack_bf16x2(dst[qc >> 1][r], dst[qc >> 1][r + 1]);
-      }
-      pf[qc] = __builtin_bit_cast(bf16x8, wp);
-      df[qc] = __builtin_bit_cast(bf16x8, wd);
-    }
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) {
-      const int drow = t * 32 + n;
-#pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        const int off = drow * (BS * 2) + t64_slot(drow, 2 * qc + h) * 16;
-        dva[t] = mfma32(*(const bf16x8*)(ots + off), pf[qc], dva[t]);
-        dka[t] = mfma32(*(const bf16x8*)(qts + off), df[qc], dka[t]);
+        const int r = 4 * g + e;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[e]));
+        if (need_mask) {
+          const int query = qb0 + ql + e;
+          if (key >= kvlen || query >= N || (CAUSAL && key > query)) pr = 0.f;
+        }
+        s[r] = pr;  // P, fp32
       }
     }
+    bf16x8 pf[2];
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[8 * qc + 2 * e], s[8 * qc + 2 * e + 1]);
+      pf[qc] = __builtin_bit_cast(bf16x8, w);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) dva[dt] = mfma32(tr_operand<D>(os, off, dt, qc), pf[qc], dva[dt]);
+    f32x16 dp;
+    zero(dp);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) dp = mfma32(*(const bf16x8*)(os + off.roff[c]), vf[c], dp);
+    __builtin_amdgcn_s_setprio(0);
+    bf16x8 df[2];
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      u32x4 w;
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int g = 2 * qc + g2;
+        const f32x4 d4 = *(const f32x4*)(st + 32 + 8 * g + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 4 * g + 2 * e;
+          w[2 * g2 + e] = pack_bf16x2(s[r] * (dp[r] - d4[2 * e]), s[r + 1] * (dp[r + 1] - d4[2 * e + 1]));
+        }
+      }
+      df[qc] = __builtin_bit_cast(bf16x8, w);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) dka[dt] = mfma32(tr_operand<D>(qs, off, dt, qc), df[qc], dka[dt]);
+    __builtin_amdgcn_s_setprio(0);
   }
+  wait_vmem();
 
   if (key < N) {
     store_rowT<D>((__bf16*)p.dk + head + (size_t)key * D, dka, p.scale, h);
@@ -355,25 +419,23 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-template <int D, int NW>
+template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
   const long long rpb = 256 / (D / 8);
   const long long g0 = (rows + rpb - 1) / rpb;
-  const long long BM = 32 * NW;
-  const long long g1 = (long long)p.B * p.H * ((p.N + BM - 1) / BM);
+  const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);
   if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
   if (p.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, true>), dim3((unsigned)g1), dim3(NW * 64), 0,
-                       stream, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, true>), dim3((unsigned)g1), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
                        p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, false>), dim3((unsigned)g1), dim3(NW * 64), 0,
-                       stream, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, false>), dim3((unsigned)g1), dim3(NW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
+                       p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
+                       p);
   }
   return hipGetLastError();
 }
@@ -382,13 +444,14 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  const size_t bytes = (size_t)B * H * N * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  const size_t rows = (size_t)B * H * N;
+  const size_t one = (rows * sizeof(float) + 255) & ~(size_t)255;
+  return 2 * one;  // D, then lse*log2(e)
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  if (p.d == 128) return launch_d<128, 4>(p, stream);
-  if (p.d == 64) return launch_d<64, 4>(p, stream);
+  if (p.d == 128) return launch_d<128>(p, stream);
+  if (p.d == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;
 }
 

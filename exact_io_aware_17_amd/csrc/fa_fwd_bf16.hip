@@ -129,14 +129,15 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   // ---- a0: tile schedule ----
   const int N = p.N;
   const int ntiles = (N + BM - 1) / BM;
-  const int G = gridDim.x;
-  const int bid = blockIdx.x;
-  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of work ids so the tiles of one head share an L2.
-  const int lid = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int bh = lid / ntiles;
-  int tile = lid % ntiles;
-  if (CAUSAL) tile = ntiles - 1 - tile;  // longest rows of a head first
+  // Tile-major order: workgroup id w takes rank w / (B*H) of head w % (B*H).
+  // Workgroups are dispatched in id order, round-robin over the 8 XCDs, so
+  // every XCD sees the heaviest tiles first (causal: the latest query rows)
+  // and, when B*H is a multiple of 8, the tiles of a fixed set of heads,
+  // whose K and V then share that XCD's L2.
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  int tile = blockIdx.x / BH;
+  if (CAUSAL) tile = ntiles - 1 - tile;
   const int b = bh / p.H;
   const int q0 = tile * BM;
 

@@ -31,6 +31,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;            // workspace: D_i = sum_c dO_ic O_ic, [B, H, N] float32
+  float* lse2;             // workspace: lse_i * log2(e) (+inf for an empty row), [B, H, N]
   const int32_t* kv_lens;
   int B, H, N, d;
   float scale;
