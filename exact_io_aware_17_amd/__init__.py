@@ -19,5 +19,7 @@ from ._lib import (  # noqa: F401
     default_scale,
     fwd,
     load,
+    schedule,
+    split_workspace_bytes,
     status_string,
 )

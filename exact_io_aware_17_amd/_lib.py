@@ -20,7 +20,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -31,10 +31,14 @@ _f = ctypes.c_float
 # Exported symbol -> (restype, argtypes), in the order include/fa.h declares them.
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "fa_fwd_split": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                          ctypes.c_size_t, _vp]),
     "fa_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                     _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _vp, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
 }
@@ -120,11 +124,58 @@ def _kv_ptr(kv_lens, B, dev):
     return kv_lens.data_ptr()
 
 
+# Zero-filled fa_fwd_split workspaces, one per device, grown on demand: every
+# completed call leaves the counter region zero; calls that share one must be
+# stream-ordered, which holds for calls on one device's current stream.
+_FWD_WS = {}
+_FWD_WS_BYTES = {}
+
+
+def split_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """fa_fwd_split_workspace_bytes for the current device (memoised per shape)."""
+    key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, B, H, N, d,
+           bool(causal))
+    n = _FWD_WS_BYTES.get(key)
+    if n is None:
+        n = int(load().fa_fwd_split_workspace_bytes(B, H, N, d,
+                                                    FA_MASK_CAUSAL if causal else FA_MASK_NONE))
+        _FWD_WS_BYTES[key] = n
+    return n
+
+
+def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    ws = _FWD_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _FWD_WS[key] = ws
+    return ws
+
+
+def schedule(N: int, BH: int, causal: bool, cus: int, occ: int):
+    """fa_fwd_schedule: (items, nslots) of fa_fwd_split's work plan (host only)."""
+    lib = load()
+    buf = (ctypes.c_uint32 * 4096)()
+    ns = ctypes.c_int(0)
+    n = lib.fa_fwd_schedule(N, BH, FA_MASK_CAUSAL if causal else FA_MASK_NONE, cus, occ, buf,
+                            4096, ctypes.byref(ns))
+    if n < 0:
+        raise FaError("fa_fwd_schedule", n, status_string(n))
+    return [int(buf[i]) for i in range(n)], int(ns.value)
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        split: bool = False, workspace: Optional[torch.Tensor] = None
         ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """fa_fwd (bfloat16) or fa_fwd_f32 (float32). Returns (O, lse)."""
+    """fa_fwd (bfloat16) or fa_fwd_f32 (float32). Returns (O, lse).
+
+    bfloat16 with split=True calls fa_fwd_split, which may split the key range
+    of heavy query tiles over several workgroups, using `workspace` (a uint8
+    device tensor whose first 64 KiB are zero, of at least
+    split_workspace_bytes(...) bytes) or, if None, a per-device cached one.
+    """
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     if scale is None:
@@ -147,10 +198,28 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     kvp = _kv_ptr(kv_lens, B, q.device)
     lib = load()
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
     with torch.cuda.device(q.device):
-        st = getattr(lib, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                                   float(scale), FA_MASK_CAUSAL if causal else FA_MASK_NONE, kvp,
-                                   _stream(q.device))
+        if fn_name == "fa_fwd_f32":
+            st = lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                float(scale), mask, kvp, _stream(q.device))
+        elif not split:
+            st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                            float(scale), mask, kvp, _stream(q.device))
+        else:
+            fn_name = "fa_fwd_split"
+            ws_ptr, ws_bytes = None, 0
+            if workspace is None:
+                need = split_workspace_bytes(B, H, N, d, causal)
+                if need > 0:
+                    workspace = _fwd_workspace(q.device, need)
+            if workspace is not None:
+                if workspace.device != q.device or not workspace.is_contiguous():
+                    raise ValueError("workspace must be a contiguous tensor on q's device")
+                ws_ptr = workspace.data_ptr()
+                ws_bytes = workspace.numel() * workspace.element_size()
+            st = lib.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                  float(scale), mask, kvp, ws_ptr, ws_bytes, _stream(q.device))
     _check(fn_name, st)
     return out, lse
 

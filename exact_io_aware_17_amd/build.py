@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
 
 # Per-source extra flags. The bf16 forward keeps its MFMA accumulators in
 # VGPRs (its rare rescale multiplies them with VALU instructions, which cannot

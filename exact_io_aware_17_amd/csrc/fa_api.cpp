@@ -33,10 +33,21 @@ float scale_log2(float scale) {
   return (float)((double)scale * 1.4426950408889634073599246810019);
 }
 
+const fa::FwdPlan& no_plan() {
+  static const fa::FwdPlan plan = [] {
+    fa::FwdPlan p{};
+    p.nitems = 0;
+    p.nslots = 0;
+    return p;
+  }();
+  return plan;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream,
-               size_t elem, bool f32) {
+               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* workspace,
+               size_t workspace_bytes, void* stream, size_t elem, bool f32) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!workspace && workspace_bytes) return FA_ERR_INVALID_ARG;
   int st = check_common(B, H, N, d, scale, mask_kind);
   if (st != FA_OK) return st;
   const size_t tbytes = (size_t)B * H * N * d * elem;
@@ -47,9 +58,16 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
               overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
     return FA_ERR_INVALID_ARG;
+  if (workspace) {
+    const void* others[5] = {q, k, v, o, lse};
+    const size_t osz[5] = {tbytes, tbytes, tbytes, tbytes, lbytes};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, workspace_bytes, others[i], osz[i])) return FA_ERR_INVALID_ARG;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_UNSUPPORTED;
   if (kv_lens && ((uintptr_t)kv_lens & 3u)) return FA_ERR_UNSUPPORTED;
+  if (workspace && !aligned16(workspace)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdParams p;
   p.q = q;
@@ -65,8 +83,30 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind == FA_MASK_CAUSAL);
-  hipError_t e = f32 ? fa::launch_fwd_f32(p, (hipStream_t)stream)
-                     : fa::launch_fwd_bf16(p, (hipStream_t)stream);
+  p.nslots = 0;
+  p.counters = nullptr;
+  p.part_ml = nullptr;
+  p.part_o = nullptr;
+  if (f32) {
+    hipError_t e = fa::launch_fwd_f32(p, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  const fa::FwdPlan* plan = &no_plan();
+  if (workspace) {
+    const int BH = B * H;
+    int cus = 0, occ = 0;
+    fa::fwd_occupancy(d, p.causal != 0, &cus, &occ);
+    const fa::FwdPlan& cand = fa::fwd_plan(N, BH, p.causal != 0, cus, occ);
+    const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, N, d);
+    if (cand.nitems > 0 && workspace_bytes >= w.total) {
+      plan = &cand;
+      p.nslots = cand.nslots;
+      p.counters = (int*)((char*)workspace + w.counters);
+      p.part_ml = (float*)((char*)workspace + w.part_ml);
+      p.part_o = (float*)((char*)workspace + w.part_o);
+    }
+  }
+  hipError_t e = fa::launch_fwd_bf16(p, *plan, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -93,12 +133,41 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, stream, 2, false);
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, nullptr, 0, stream, 2,
+                    false);
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int mask_kind) {
+  if (check_common(B, H, N, d, 1.f, mask_kind) != FA_OK) return 0;
+  const bool causal = (mask_kind == FA_MASK_CAUSAL);
+  int cus = 0, occ = 0;
+  fa::fwd_occupancy(d, causal, &cus, &occ);
+  const fa::FwdPlan& plan = fa::fwd_plan(N, B * H, causal, cus, occ);
+  return fa::fwd_workspace_layout(plan, B * H, N, d).total;
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, workspace,
+                    workspace_bytes, stream, 2, false);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, stream, 4, true);
+  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, nullptr, 0, stream, 4,
+                    true);
+}
+
+int fa_fwd_schedule(int N, int BH, int mask_kind, int cus, int occ, uint32_t* items,
+                    int max_items, int* nslots) {
+  if (N <= 0 || BH <= 0 || cus < 0 || occ < 0 || max_items < 0 || (max_items > 0 && !items))
+    return FA_ERR_INVALID_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
+  const fa::FwdPlan& plan = fa::fwd_plan(N, BH, mask_kind == FA_MASK_CAUSAL, cus, occ);
+  for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
+  if (nslots) *nslots = plan.nslots;
+  return plan.nitems;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

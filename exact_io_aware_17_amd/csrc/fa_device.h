@@ -94,6 +94,24 @@ __device__ __forceinline__ float add_bf16_pair(unsigned w, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
+// Raw buffer resource over `base` (byte offsets up to 2^31 - 1, no bounds
+// checking beyond that; the caller keeps offsets inside its allocation).
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+__device__ __forceinline__ buffer_rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// Device-coherent 16-byte store / load (cache policy sc1, the encoding of
+// agent-scope atomic accesses): visible to every XCD without a cache-wide
+// write-back or invalidation.
+constexpr int CPOL_SC1 = 16;
+__device__ __forceinline__ void store_coherent16(f32x4 v, buffer_rsrc r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ f32x4 load_coherent16(buffer_rsrc r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+
 __device__ __forceinline__ void zero(f32x16& x) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = 0.f;

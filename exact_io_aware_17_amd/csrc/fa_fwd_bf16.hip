@@ -44,10 +44,21 @@
 //    straddle the diagonal or the padding length apply a mask.
 //  * A row with no visible key keeps l = 0 and is written as O = 0 and
 //    lse = -inf ("Worked examples", Cell D2).
+//  * Load balance: a host plan may cut a tile's key range into up to four
+//    parts processed by different workgroups. Each part stores its partial
+//    state (unnormalised O, reference max, both sums; fp32) and counts its
+//    arrival on the tile's counter; the last part to arrive merges all parts
+//    in part order with the exact block merge ("Exercises", the block
+//    merges), so the result does not depend on which part finished last,
+//    and resets the counter to zero. No workgroup ever waits for another.
 #include "fa_internal.h"
 #include "fa_device.h"
 
 #include <math.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace fa {
 namespace {
@@ -56,10 +67,11 @@ using namespace dev;
 
 constexpr int NW = 4;         // waves per workgroup
 constexpr int BM = 32 * NW;   // queries per workgroup
+static_assert(BM == FWD_BM, "workgroup tile matches the host planner");
 constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
 
 #ifndef FA_FWD_BN
-#define FA_FWD_BN 32
+#define FA_FWD_BN FWD_BN
 #endif
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 2
@@ -103,7 +115,7 @@ __device__ __forceinline__ void wait_vmem_upto(bool allow_k) {
 }
 
 template <int D, int BN, int STAGES, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p, FwdPlan plan) {
   constexpr int ROWB = D * 2;                 // bytes per K/V row
   constexpr int TILE = BN * ROWB;             // bytes per K or V tile
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
@@ -119,6 +131,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
   __shared__ __attribute__((aligned(1024))) char kbuf[STAGES][TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[STAGES][TILE];
+  __shared__ int s_arrival;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,18 +139,26 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   const int n = lane & 31;  // query of this lane within the wave / row within an MFMA tile
   const int h = lane >> 5;  // lane half
 
-  // ---- a0: tile schedule ----
+  // ---- a0: work item ----
   const int N = p.N;
   const int ntiles = (N + BM - 1) / BM;
-  // Tile-major order: workgroup id w takes rank w / (B*H) of head w % (B*H).
+  // Item-major order: workgroup id w takes item w / (B*H) of head w % (B*H).
   // Workgroups are dispatched in id order, round-robin over the 8 XCDs, so
-  // every XCD sees the heaviest tiles first (causal: the latest query rows)
-  // and, when B*H is a multiple of 8, the tiles of a fixed set of heads,
-  // whose K and V then share that XCD's L2.
+  // every XCD sees the heaviest items first and, when B*H is a multiple of
+  // 8, the items of a fixed set of heads, whose K and V then share its L2.
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  int tile = blockIdx.x / BH;
-  if (CAUSAL) tile = ntiles - 1 - tile;
+  const int rank = blockIdx.x / BH;
+  int tile, part = 0, nparts = 1, slot_base = 0;
+  if (plan.nitems > 0) {
+    const unsigned it = plan.item[rank];
+    tile = (int)(it & 0xffffu);
+    part = (int)((it >> 16) & 3u);
+    nparts = (int)((it >> 18) & 3u) + 1;
+    slot_base = (int)(it >> 20);
+  } else {
+    tile = CAUSAL ? ntiles - 1 - rank : rank;  // causal: the latest rows see the most keys
+  }
   const int b = bh / p.H;
   const int q0 = tile * BM;
 
@@ -145,7 +166,12 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
   int kend = kvlen;
   if (CAUSAL) kend = min(kend, q0 + BM);
-  const int nblk = (kend + BN - 1) / BN;
+  const int nblk = (kend + BN - 1) / BN;  // visible blocks
+  // This item's block range: its share of the tile's nominal (unpadded)
+  // blocks, clipped to the visible ones.
+  const int nbn = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
+  const int jbeg = part * nbn / nparts;
+  const int jend = min((part + 1) * nbn / nparts, nblk);
   const int qa = q0 + wave * 32;  // first query of this wave
   const int qrow = qa + n;
 
@@ -166,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
   // ---- a1: K/V block stream, HBM -> LDS ----
   auto issue_block = [&](int j) {
-    if (j >= nblk) return;
+    if (j >= jend) return;
     const int key0 = j * BN;
     char* ks = kbuf[j % STAGES];
     char* vs = vbuf[j % STAGES];
@@ -205,12 +231,12 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   float l_bf = 0.f;       // the same over the bf16-rounded p used by P V
   const float scl = p.scale_log2;
 
-  // Prologue: blocks 0 .. STAGES-2 in flight.
+  // Prologue: the first STAGES-1 blocks in flight.
 #pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j) issue_block(j);
+  for (int j = 0; j < STAGES - 1; ++j) issue_block(jbeg + j);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int j = 0; j < nblk; ++j) {
+  for (int j = jbeg; j < jend; ++j) {
     // Block j has landed once at most the DMAs of the blocks issued after it
     // (j+1 .. j+STAGES-2) are outstanding; this wave's only vector-memory
     // instructions from here on are these DMAs.
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
       wait_vmem_upto<0>(false);
     } else {
       static_assert(STAGES == 3, "ring of 2 or 3 stages");
-      wait_vmem_upto<2 * DPW>(j + 1 < nblk);
+      wait_vmem_upto<2 * DPW>(j + 1 < jend);
     }
     __syncthreads();               // all waves: block j landed, block j-1's stage is free
     issue_block(j + STAGES - 1);   // into the stage block j-1 used
@@ -313,6 +339,70 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   __builtin_amdgcn_s_setprio(0);
   wait_vmem();  // no DMA may still target this workgroup's LDS at exit
 
+  // ---- split item: publish the partial state; the last arrival merges ----
+  if (nparts > 1) {
+    // Slot layout (fp32): accumulators as [wave][dt][r/4][lane][r%4] (every
+    // 16-byte access of a wave covers 1 KB contiguously), then per lane
+    // {m, l, l_bf, 0}. Written and read with device-coherent 16-byte buffer
+    // accesses (they bypass the per-XCD L2 caches), so no cache-wide
+    // write-back or invalidation is needed; completing this wave's stores
+    // before the barrier orders them before the arrival count.
+    constexpr int SLOT_O = BM * D * 4;              // bytes of accumulators per slot
+    constexpr int SLOT_ML = FWD_ML_FLOATS * 4;      // bytes of row statistics per slot
+    const size_t slot0 = (size_t)bh * p.nslots + slot_base;
+    const buffer_rsrc ro = make_rsrc(p.part_o + slot0 * (BM * D));
+    const buffer_rsrc rm = make_rsrc(p.part_ml + slot0 * FWD_ML_FLOATS);
+    const int vo = (wave * DT * 4 * 64 + lane) * 16;  // + ((dt * 4 + g) * 64) * 16
+    const int vm = (wave * 64 + lane) * 16;
+    {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+          store_coherent16(v, ro, part * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
+        }
+      const f32x4 st = {m_run, l_run, l_bf, 0.f};
+      store_coherent16(st, rm, part * SLOT_ML + vm);
+    }
+    wait_vmem();
+    __syncthreads();
+    int* ctr = p.counters + (size_t)bh * ntiles + tile;
+    if (tid == 0) s_arrival = atomicAdd(ctr, 1);
+    __syncthreads();
+    if (s_arrival != nparts - 1) return;  // another part will merge
+    if (tid == 0) atomicExch(ctr, 0);     // ready for the next call
+
+    // Every part, this one included, is read back and combined in part
+    // order: the result does not depend on which part arrived last.
+    f32x4 stat[4];
+    float m_all = NEG_INF;
+    for (int q = 0; q < nparts; ++q) {
+      stat[q] = load_coherent16(rm, q * SLOT_ML + vm);
+      m_all = fmaxf(m_all, stat[q][0]);
+    }
+    float l_sum = 0.f, lbf_sum = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
+    for (int q = 0; q < nparts; ++q) {
+      const float m_q = stat[q][0];
+      const float c = (m_q == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_q - m_all);
+      l_sum = fmaf(c, stat[q][1], l_sum);
+      lbf_sum = fmaf(c, stat[q][2], lbf_sum);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = load_coherent16(ro, q * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dt][4 * g + e] = fmaf(c, v[e], acc[dt][4 * g + e]);
+        }
+    }
+    m_run = m_all;
+    l_run = l_sum;
+    l_bf = lbf_sum;
+  }
+
   // ---- a6: finalize ----
   const float l_tot = pair_sum(l_run);
   const float l_o = pair_sum(l_bf);
@@ -336,26 +426,61 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
   constexpr int BN = FA_FWD_BN, ST = FA_FWD_STAGES;
+  static_assert(BN == FWD_BN, "the host planner counts blocks of FWD_BN keys");
   const long long ntiles = (p.N + BM - 1) / BM;
-  const long long grid = (long long)p.B * p.H * ntiles;
+  const long long items = plan.nitems > 0 ? plan.nitems : ntiles;
+  const long long grid = (long long)p.B * p.H * items;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p);
+                       stream, p, plan);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, false>), dim3((unsigned)grid), dim3(NW * 64),
-                       0, stream, p);
+                       0, stream, p, plan);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+int occupancy() {
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per, reinterpret_cast<const void*>(&fwd_bf16_kernel<D, FA_FWD_BN, FA_FWD_STAGES, CAUSAL>),
+          NW * 64, 0) != hipSuccess)
+    return 0;
+  return per;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 128) return launch_d<128>(p, stream);
-  if (p.d == 64) return launch_d<64>(p, stream);
+hipError_t launch_fwd_bf16(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+  if (p.d == 128) return launch_d<128>(p, plan, stream);
+  if (p.d == 64) return launch_d<64>(p, plan, stream);
   return hipErrorInvalidValue;
+}
+
+void fwd_occupancy(int d, bool causal, int* cus_out, int* occ_out) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, bool>, std::pair<int, int>> cache;
+  *cus_out = 0;
+  *occ_out = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, d, causal);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+    if (d == 128) per = causal ? occupancy<128, true>() : occupancy<128, false>();
+    if (d == 64) per = causal ? occupancy<64, true>() : occupancy<64, false>();
+    if (cus <= 0 || per <= 0) cus = per = 0;
+    it = cache.emplace(key, std::make_pair(cus, per)).first;
+  }
+  *cus_out = it->second.first;
+  *occ_out = it->second.second;
 }
 
 }  // namespace fa

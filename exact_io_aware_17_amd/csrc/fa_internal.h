@@ -18,7 +18,49 @@ struct FwdParams {
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
   int causal;
+  // Split work items (used only with a plan of nitems > 0): per (b, h)
+  // nslots partial states, each BM rows of unnormalised O (fp32) plus the
+  // row max and both row sums, and one arrival counter per query tile.
+  int nslots;
+  int* counters;           // FWD_COUNTERS ints, zero between calls; [B*H, ntiles] used
+  float* part_ml;          // [B*H, nslots, FWD_ML_FLOATS]
+  float* part_o;           // [B*H, nslots, FWD_BM * d]
 };
+
+// Forward tiling shared by the kernel and the host planner.
+constexpr int FWD_BM = 128;                 // query rows per workgroup
+constexpr int FWD_BN = 32;                  // keys per streamed block
+constexpr int FWD_ML_FLOATS = 4 * 2 * FWD_BM;  // {m, l, l_bf, 0} for each of 2*BM lanes
+constexpr int FWD_PLAN_MAX = 512;
+// Arrival counters occupy a fixed region at the start of every forward
+// workspace, whatever the shape, so a workspace reused for another shape
+// still finds them zero: plans are made only when B*H*ntiles fits.
+constexpr int FWD_COUNTERS = 16384;
+
+// Work items of the forward, in dispatch order (the same list for every
+// (b, h)). Item: tile | part << 16 | (nparts - 1) << 18 | slot_base << 20.
+// Part `part` of `nparts` covers key blocks [part*nb/nparts, (part+1)*nb/nparts)
+// of the tile's nb nominal blocks; split parts use partial-state slots
+// slot_base + part.
+struct FwdPlan {
+  int nitems;  // 0: one item per tile, heaviest first (no split)
+  int nslots;  // partial-state slots per (b, h)
+  uint32_t item[FWD_PLAN_MAX];
+};
+
+// Balancing plan for N query rows, BH heads, `cus` compute units and `occ`
+// resident workgroups per compute unit (cached; the reference stays valid).
+const FwdPlan& fwd_plan(int N, int BH, bool causal, int cus, int occ);
+// Nominal key blocks of query tile t.
+int fwd_tile_blocks(int N, int t, bool causal);
+// Workspace layout for a plan: byte offsets of counters, part_ml, part_o and the total.
+struct FwdWorkspace {
+  size_t counters, part_ml, part_o, total;
+};
+FwdWorkspace fwd_workspace_layout(const FwdPlan& plan, int BH, int N, int d);
+// Compute units of the current device and resident forward workgroups per
+// compute unit (both 0 if unknown).
+void fwd_occupancy(int d, bool causal, int* cus, int* occ);
 
 struct BwdParams {
   const void* q;
@@ -40,7 +82,7 @@ struct BwdParams {
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdParams& p, const FwdPlan& plan, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 

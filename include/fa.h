@@ -23,8 +23,9 @@
  *
  * Layout: every tensor is contiguous [B, H, N, d] (d innermost), lse is
  * contiguous [B, H, N] float32. Pointers are device pointers allocated by
- * the caller (the library allocates and frees nothing and keeps no mutable
- * state). Tensor base pointers must be 16-byte aligned.
+ * the caller (the library allocates and frees no device memory; on the host
+ * it caches per-shape work plans and per-device occupancy, guarded by a
+ * mutex). Tensor and workspace base pointers must be 16-byte aligned.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -74,11 +75,45 @@ typedef enum {
  *   kv_lens : device int32 [B] valid key counts, or NULL
  *   stream  : hipStream_t
  * Products Q K^T and P V run on bf16 matrix cores with float32 accumulation;
- * P is rounded to bfloat16 before the P V product.
+ * P is rounded to bfloat16 before the P V product. One workgroup computes
+ * each block of 128 query rows over all of its visible keys.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int mask_kind,
            const int32_t* kv_lens, void* stream);
+
+/*
+ * Bytes of workspace fa_fwd_split needs for these sizes on the current
+ * device; 0 when its plan does not split any tile (then fa_fwd_split is
+ * fa_fwd), or for invalid arguments.
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int mask_kind);
+
+/*
+ * fa_fwd with the key range of the heaviest query tiles split over several
+ * workgroups (split-KV): each part streams its share of the keys, stores its
+ * partial softmax state (row max, both row sums, unnormalised output; fp32)
+ * in the workspace, and the last part of a tile to finish merges all parts
+ * with the exact block merge ("Exercises" of the interactive explainer "The
+ * Flash Attention", the block merges) in part order. For grids too small to
+ * fill the GPU (few heads, long rows) this spreads a tile over several
+ * compute units. Same tensors and results as fa_fwd up to rounding; bitwise
+ * reproducible for a given device and shape.
+ *   workspace       : device memory, or NULL with workspace_bytes = 0. With
+ *                     fewer than fa_fwd_split_workspace_bytes(...) bytes no
+ *                     tile is split. Its first 64 KiB hold arrival counters
+ *                     that must be zero before the first use; every completed
+ *                     call leaves them zero, for any later shape (the rest is
+ *                     scratch). Calls sharing a workspace must be ordered
+ *                     (same stream, or synchronised). It must not overlap any
+ *                     tensor argument.
+ * Errors as fa_fwd, and FA_ERR_INVALID_ARG for workspace_bytes > 0 with a
+ * NULL workspace, FA_ERR_UNSUPPORTED for a workspace not 16-byte aligned.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int mask_kind,
+                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * The same contract with float32 q, k, v, o (float32 arithmetic throughout).
@@ -109,6 +144,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, void* dq, void* dk, void* dv, void* workspace,
            int B, int H, int N, int d, float scale, int mask_kind,
            const int32_t* kv_lens, void* stream);
+
+/*
+ * Host-only view of fa_fwd_split's work plan (no device call): for N query
+ * rows, BH = B*H heads, mask_kind, `cus` compute units and `occ` resident
+ * workgroups per compute unit, returns the number of work items (0 = one
+ * item per query tile, no split) and copies up to max_items of them to
+ * `items`, each
+ *   tile | part << 16 | (nparts - 1) << 18 | slot_base << 20,
+ * in dispatch order; *nslots receives the partial-state slots per head.
+ * Returns FA_ERR_INVALID_ARG for invalid arguments.
+ */
+int fa_fwd_schedule(int N, int BH, int mask_kind, int cus, int occ, uint32_t* items,
+                    int max_items, int* nslots);
 
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);

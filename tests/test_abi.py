@@ -49,12 +49,14 @@ def test_workspace_bytes():
 
 
 def _fwd(fn="fa_fwd", q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ,
-         B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
+         B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None, ws=None, ws_bytes=0):
     lib = _lib.load()
+    if fn == "fa_fwd_split":
+        return lib.fa_fwd_split(q, k, v, o, lse, B, H, N, d, scale, mask, kv, ws, ws_bytes, None)
     return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, scale, mask, kv, None)
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_split", "fa_fwd_f32"])
 def test_fwd_argument_errors(fn):
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
     assert _fwd(fn, q=None) == INV
@@ -74,6 +76,23 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, q=A + 2) == UNS                 # not 16-byte aligned
     assert _fwd(fn, kv=A + 5 * SZ + 2) == UNS       # kv_lens not 4-byte aligned
     assert _fwd(fn, B=1 << 16, H=1 << 16, N=1) == UNS  # row count beyond 32-bit
+
+
+def test_split_workspace_argument_errors():
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    f = "fa_fwd_split"
+    assert _fwd(f, ws=None, ws_bytes=256) == INV            # size without a pointer
+    assert _fwd(f, ws=A + 16, ws_bytes=SZ) == INV           # workspace overlaps q
+    assert _fwd(f, ws=A + 3 * SZ + 64, ws_bytes=256) == INV  # workspace overlaps o
+    assert _fwd(f, ws=A + 6 * SZ + 4, ws_bytes=256) == UNS  # not 16-byte aligned
+    assert _fwd(f, ws=A + 6 * SZ + 4, ws_bytes=256, B=0) == INV
+
+
+def test_split_workspace_bytes_invalid_sizes():
+    lib = _lib.load()
+    assert lib.fa_fwd_split_workspace_bytes(0, 16, 4096, 128, 1) == 0
+    assert lib.fa_fwd_split_workspace_bytes(2, 16, 4096, 96, 1) == 0
+    assert lib.fa_fwd_split_workspace_bytes(2, 16, 4096, 128, 7) == 0
 
 
 def test_bwd_argument_errors():

@@ -1,0 +1,107 @@
+"""GPU parity of fa_fwd_split (split-KV): the heaviest query tiles cut into key
+ranges whose partial states are merged by the last part to arrive.
+
+Both entry points (fa_fwd_split, and fa_fwd with one workgroup per tile) are
+compared with the fp64 oracle on the same inputs; the split path must be
+bitwise reproducible and must leave its arrival counters at zero. The shapes
+have few heads, so that the plan splits them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_17_amd as fa
+
+from _parity import BF16_LSE_ABS, BF16_LSE_REL, BF16_O_MAX, BF16_O_MEAN, check_lse, check_o, \
+    oracle_fwd, say, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# (B, H, N, d, causal, kv_lens)
+CASES = [
+    (1, 1, 1024, 128, False, None),       # every tile in 4 parts
+    (1, 2, 768, 64, True, [700]),
+    (2, 3, 1000, 128, True, None),        # ragged last tile
+    (2, 2, 640, 64, False, [0, 333]),     # an empty batch and parts beyond kv_len
+    (1, 2, 4096, 128, True, None),
+    (2, 1, 2048, 128, True, [2048, 700]),
+]
+
+
+def _inputs(B, H, N, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(3))
+    return q, k, v
+
+
+def _ids(c):
+    B, H, N, d, causal, kv = c
+    return f"B{B}H{H}N{N}d{d}{'c' if causal else ''}{'' if kv is None else 'kv'}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_split_and_unsplit_match_oracle(case):
+    B, H, N, d, causal, kvl = case
+    say(f"case split B={B} H={H} N={N} d={d} causal={causal} kv_lens={kvl}")
+    need = fa.split_workspace_bytes(B, H, N, d, causal)
+    assert need > 0, "the plan was expected to split this shape"
+    q, k, v = _inputs(B, H, N, d, 1700 + N + d)
+    kv = None if kvl is None else torch.tensor(kvl, dtype=torch.int32)
+    kvd = None if kv is None else kv.to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    scale = fa.default_scale(d)
+    o_s, lse_s = fa.fwd(qd, kd, vd, causal=causal, scale=scale, kv_lens=kvd, split=True,
+                        workspace=ws)
+    o_u, lse_u = fa.fwd(qd, kd, vd, causal=causal, scale=scale, kv_lens=kvd)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_fwd(q, k, v, scale, causal, kv)
+    for o, lse in ((o_s, lse_s), (o_u, lse_u)):
+        check_o(to64(o), o_ref, BF16_O_MAX, BF16_O_MEAN)
+        check_lse(to64(lse), lse_ref, BF16_LSE_ABS, BF16_LSE_REL)
+    # The arrival counters (first 64 KiB of the workspace) are back at zero.
+    assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_split_is_bitwise_reproducible_and_reusable():
+    B, H, N, d = 1, 4, 4096, 128
+    say(f"case split-repeat B={B} H={H} N={N} d={d}")
+    need = fa.split_workspace_bytes(B, H, N, d, True)
+    assert need > 0
+    q, k, v = (t.to(DEV) for t in _inputs(B, H, N, d, 1717))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    outs = [fa.fwd(q, k, v, causal=True, split=True, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0])
+        assert torch.equal(lse, outs[0][1])
+    # A smaller shape on the same (larger) workspace right after, whose
+    # counters would overlap the first shape's partial states if they were
+    # laid out per shape.
+    q2, k2, v2 = (t[:1, :2, :1000].contiguous() for t in (q, k, v))
+    assert 0 < fa.split_workspace_bytes(1, 2, 1000, d, True) <= need
+    o2, lse2 = fa.fwd(q2, k2, v2, causal=True, split=True, workspace=ws)
+    o2u, lse2u = fa.fwd(q2, k2, v2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(o2.float() - o2u.float())).item() <= 2 * BF16_O_MAX
+    assert torch.max(torch.abs(lse2 - lse2u)).item() <= 2e-3
+
+
+def test_short_workspace_runs_unsplit():
+    B, H, N, d = 1, 2, 1024, 128
+    need = fa.split_workspace_bytes(B, H, N, d, True)
+    assert need > 0
+    q, k, v = (t.to(DEV) for t in _inputs(B, H, N, d, 1718))
+    short = torch.zeros(need - 256, dtype=torch.uint8, device=DEV)
+    o_a, lse_a = fa.fwd(q, k, v, causal=True, split=True, workspace=short)
+    o_b, lse_b = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(lse_a, lse_b)
+    assert int(short.abs().sum().item()) == 0  # untouched
+
+
+def test_metric_shape_is_not_split():
+    # Several waves of workgroups: fa_fwd_split runs one workgroup per tile.
+    assert fa.split_workspace_bytes(2, 16, 4096, 128, True) == 0
