@@ -22,9 +22,11 @@
 //    transpose read (ds_read_b64_tr_b16): four lanes reading four key rows
 //    give each lane four keys of one d column.
 //  * K and V tiles go from HBM to LDS with direct 16-byte loads (no register
-//    staging) through a ring of STAGES buffers: block j+STAGES-1 is in flight
-//    while block j is used. 16-byte chunks are XOR-swizzled per row so the
-//    operand reads hit every LDS bank evenly.
+//    staging) into two buffers: block j+1 is in flight while block j is
+//    used. 16-byte chunks are XOR-swizzled per row so the operand reads hit
+//    every LDS bank evenly. The loop is unrolled by two so that each
+//    buffer's LDS offsets are immediates, and each lane's source offsets
+//    within a block are computed once.
 //  * Registers are kept low enough for several waves per SIMD: their
 //    interleaving hides LDS and MFMA latency and overlaps one wave's softmax
 //    with another's matrix work.
@@ -59,6 +61,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -103,17 +106,6 @@ __device__ __forceinline__ int vswz(int row) {
   }
 }
 
-// s_waitcnt vmcnt(n) for n = 0 or n = K (K a compile-time count <= 15).
-template <int K>
-__device__ __forceinline__ void wait_vmem_upto(bool allow_k) {
-  static_assert(K <= 15, "vmcnt immediate must fit the low field");
-  if (allow_k) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | K);
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
-}
-
 template <int D, int BN, int STAGES, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p, FwdPlan plan) {
   constexpr int ROWB = D * 2;                 // bytes per K/V row
@@ -128,6 +120,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   constexpr int KC = BN / 16;                 // 16-key contraction chunks per block
   static_assert(DMA_PER_TILE % NW == 0, "DMA blocks must split evenly over the waves");
   static_assert(BN == 32 || BN == 64, "block of 32 or 64 keys");
+  static_assert(STAGES == 2, "double-buffered K/V stream");
 
   __shared__ __attribute__((aligned(1024))) char kbuf[STAGES][TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf[STAGES][TILE];
@@ -135,7 +128,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int n = lane & 31;  // query of this lane within the wave / row within an MFMA tile
   const int h = lane >> 5;  // lane half
 
@@ -191,19 +184,42 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- a1: K/V block stream, HBM -> LDS ----
-  auto issue_block = [&](int j) {
+  // Per-lane source offsets inside a block (bytes), fixed for the kernel: a
+  // block's DMA then needs only a scalar base. A block that runs past row
+  // N-1 (the ragged end) takes the clamped path.
+  int gk[DPW], gv[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int row = (wave * DPW + i) * ROWS_PER_DMA + lane / CPR;
+    const int pch = lane % CPR;
+    gk[i] = row * ROWB + (pch ^ kswz<D>(row)) * 16;
+    gv[i] = row * ROWB + (pch ^ vswz<D>(row)) * 16;
+  }
+  auto issue_block = [&](int j, auto stage) {
+    constexpr int SD = decltype(stage)::value;
     if (j >= jend) return;
     const int key0 = j * BN;
-    char* ks = kbuf[j % STAGES];
-    char* vs = vbuf[j % STAGES];
+    char* ks = kbuf[SD];
+    char* vs = vbuf[SD];
+    if (key0 + BN <= N) {
+      const char* kb = (const char*)(K + (size_t)key0 * D);
+      const char* vb = (const char*)(V + (size_t)key0 * D);
 #pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int blk = wave * DPW + i;
-      const int row = blk * ROWS_PER_DMA + lane / CPR;
-      const int pch = lane % CPR;
-      const size_t key = (size_t)min(key0 + row, N - 1);
-      dma16(K + key * D + (pch ^ kswz<D>(row)) * 8, ks + blk * 1024);
-      dma16(V + key * D + (pch ^ vswz<D>(row)) * 8, vs + blk * 1024);
+      for (int i = 0; i < DPW; ++i) {
+        const int blk = wave * DPW + i;
+        dma16(kb + gk[i], ks + blk * 1024);
+        dma16(vb + gv[i], vs + blk * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int blk = wave * DPW + i;
+        const int row = blk * ROWS_PER_DMA + lane / CPR;
+        const int pch = lane % CPR;
+        const size_t key = (size_t)min(key0 + row, N - 1);
+        dma16(K + key * D + (pch ^ kswz<D>(row)) * 8, ks + blk * 1024);
+        dma16(V + key * D + (pch ^ vswz<D>(row)) * 8, vs + blk * 1024);
+      }
     }
   };
 
@@ -231,29 +247,23 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   float l_bf = 0.f;       // the same over the bf16-rounded p used by P V
   const float scl = p.scale_log2;
 
-  // Prologue: the first STAGES-1 blocks in flight.
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j) issue_block(jbeg + j);
-  __builtin_amdgcn_sched_barrier(0);
-
-  for (int j = jbeg; j < jend; ++j) {
-    // Block j has landed once at most the DMAs of the blocks issued after it
-    // (j+1 .. j+STAGES-2) are outstanding; this wave's only vector-memory
-    // instructions from here on are these DMAs.
-    if constexpr (STAGES == 2) {
-      wait_vmem_upto<0>(false);
-    } else {
-      static_assert(STAGES == 3, "ring of 2 or 3 stages");
-      wait_vmem_upto<2 * DPW>(j + 1 < jend);
-    }
-    __syncthreads();               // all waves: block j landed, block j-1's stage is free
-    issue_block(j + STAGES - 1);   // into the stage block j-1 used
+  // One key block: the stage (LDS buffer) is a compile-time constant, so
+  // every LDS operand offset is an immediate. Block j uses stage
+  // (j - jbeg) % 2; the DMA of block j+1 goes to the other stage.
+  auto step = [&](int j, auto stage) {
+    constexpr int ST = decltype(stage)::value;
+    // Block j has landed once this wave's DMAs are done (its only
+    // outstanding vector-memory operations) and every wave has passed the
+    // barrier, which also frees the other stage, read in block j-1.
+    wait_vmem();
+    __syncthreads();
+    issue_block(j + 1, std::integral_constant<int, 1 - ST>());
 
     const int key0 = j * BN;
     // Skip blocks wholly in this wave's future (all its rows would be masked).
-    if (CAUSAL && key0 > qa + 31) continue;
-    const char* ks = kbuf[j % STAGES];
-    const char* vs = vbuf[j % STAGES];
+    if (CAUSAL && key0 > qa + 31) return;
+    const char* ks = kbuf[ST];
+    const char* vs = vbuf[ST];
 
     // ---- a2: S^T = K Q^T for BN keys x 32 queries ----
     // Waves in a matrix phase get issue priority over waves in their softmax,
@@ -335,6 +345,13 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
             __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = mfma32(a, pf[kc], acc[dt]);
       }
+  };
+
+  issue_block(jbeg, std::integral_constant<int, 0>());
+  __builtin_amdgcn_sched_barrier(0);
+  for (int j = jbeg; j < jend; j += 2) {
+    step(j, std::integral_constant<int, 0>());
+    if (j + 1 < jend) step(j + 1, std::integral_constant<int, 1>());
   }
   __builtin_amdgcn_s_setprio(0);
   wait_vmem();  // no DMA may still target this workgroup's LDS at exit
