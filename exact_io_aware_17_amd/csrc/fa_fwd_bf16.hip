@@ -72,6 +72,7 @@ constexpr int NW = 4;         // waves per workgroup
 constexpr int BM = 32 * NW;   // queries per workgroup
 static_assert(BM == FWD_BM, "workgroup tile matches the host planner");
 constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
+constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 
 #ifndef FA_FWD_BN
 #define FA_FWD_BN FWD_BN
@@ -294,14 +295,41 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     }
 
     // ---- a4: online softmax ----
-    float mx = NEG_INF;
+    // Probabilities against the current reference max m_run. While the
+    // block's row max stays within TAU of it every p is at most 2^TAU, so a
+    // lane sum above 2^TAU (or not a number: m_run = -inf at the start) is
+    // the only case that needs the block max: then the reference moves to
+    // the row's block max if that lies more than TAU above it (rescaling the
+    // accumulators once), and the block's p are recomputed.
+    bf16x8 pf[KC];
+    float rs, lbf_blk;
+    auto probabilities = [&](float m_use) {
+      rs = 0.f;
+      lbf_blk = 0.f;
 #pragma unroll
-    for (int t = 0; t < KT; ++t)
+      for (int kc = 0; kc < KC; ++kc) {
+        u32x4 w;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    const float mt = pair_max(mx) * scl;  // block max, scaled (-inf if all hidden)
-    const bool up = mt > m_run + TAU;
-    if (__any(up)) {
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * (kc & 1) + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], scl, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r + 1], scl, -m_use));
+          w[e] = pack_bf16x2(p0, p1);
+          rs += p0 + p1;
+          lbf_blk = add_bf16_pair(w[e], lbf_blk);
+        }
+        pf[kc] = __builtin_bit_cast(bf16x8, w);
+      }
+    };
+    probabilities(m_run);
+    if (__any(!(rs <= P_BOUND))) {
+      float mx = NEG_INF;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      const float mt = pair_max(mx) * scl;  // block max, scaled (-inf if all hidden)
+      const bool up = mt > m_run + TAU;
       const float m_new = up ? mt : m_run;
       const float corr = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
       l_run *= corr;
@@ -311,27 +339,10 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
       m_run = m_new;
-    }
-    const float m_use = (m_run == NEG_INF) ? 0.f : m_run;  // nothing visible yet: p = 0
-
-    // P^T fragments (bf16): chunk kc = registers 8*(kc%2) .. +8 of tile kc/2.
-    bf16x8 pf[KC];
-    float rs = 0.f;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * (kc & 1) + 2 * e;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], scl, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r + 1], scl, -m_use));
-        w[e] = pack_bf16x2(p0, p1);
-        rs += p0 + p1;
-        l_bf = add_bf16_pair(w[e], l_bf);
-      }
-      pf[kc] = __builtin_bit_cast(bf16x8, w);
+      probabilities((m_run == NEG_INF) ? 0.f : m_run);  // nothing visible yet: p = 0
     }
     l_run += rs;
+    l_bf += lbf_blk;
 
     __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
     // ---- a5: O^T += V^T P^T ----
