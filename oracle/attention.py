@@ -22,7 +22,8 @@ Readings taken where the pages leave a step open (each is listed with the
 design notes of this repository):
 
 * causal means key j is visible to query i iff j <= i (top-left aligned,
-  N_q = N_k); the strict variant (j < i) of Cell D2 is only a test device;
+  N_q = N_k); the strict variant (j < i), which the pages use in Cell D2 to
+  produce a row with no visible key, is selected with causal="strict";
 * key padding kv_lens[b] hides keys j >= kv_lens[b] for every query of batch
   b; queries are never dropped;
 * the merge of two states whose maxima are both -inf keeps the empty state
@@ -184,21 +185,27 @@ def _as_f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def visible(n_rows: int, n_keys: int, causal: bool, kv_len: int,
+def visible(n_rows: int, n_keys: int, causal, kv_len: int,
             rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Boolean [len(rows), n_keys]: key j visible to query i.
 
-    Visible iff (not causal or j <= i) and j < kv_len. Causal masking follows
-    "Worked examples", Cell D (keys in the query's future are hidden); the
-    key-padding length is this repository's reading for batched, padded
-    inputs (keys only are padded).
+    causal is False (no mask), True (j <= i) or "strict" (j < i). Visible iff
+    the causal condition holds and j < kv_len. Causal masking follows "Worked
+    examples", Cell D (keys in the query's future are hidden); the strict
+    form, which also hides the query's own position, is the variant of Cell
+    D2; the key-padding length is this repository's reading for batched,
+    padded inputs (keys only are padded).
     """
+    if causal not in (False, True, "strict"):
+        raise ValueError("causal must be False, True or 'strict'")
     if rows is None:
         rows = np.arange(n_rows)
     i = np.asarray(rows)[:, None]
     j = np.arange(n_keys)[None, :]
     vis = j < kv_len
-    if causal:
+    if causal == "strict":
+        vis = vis & (j < i)
+    elif causal:
         vis = vis & (j <= i)
     return vis
 
@@ -216,7 +223,8 @@ def attn_fwd_naive(q, k, v, scale: float, causal: bool = False, kv_lens=None,
 
     q, k, v: [B, H, N, d] (any float dtype; upcast to float64 losslessly).
     scale: the caller's scale (tests pass the float32 value the GPU receives).
-    causal: hide keys j > i. kv_lens: None or per-batch valid key counts.
+    causal: False, True (hide keys j > i) or "strict" (hide keys j >= i).
+    kv_lens: None or per-batch valid key counts.
     rows: optional query indices to compute (rows are independent, so this is
     the same definition restricted to those rows).
     heads: optional list of (b, h) to compute; others are left as NaN.

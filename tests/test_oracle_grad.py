@@ -17,7 +17,8 @@ def _loss(q, k, v, do, scale, causal, kv_lens):
     return float(np.sum(do * o))
 
 
-@pytest.mark.parametrize("causal,kv_lens", [(False, None), (True, None), (True, [0, 11])])
+@pytest.mark.parametrize("causal,kv_lens", [(False, None), (True, None), (True, [0, 11]),
+                                            ("strict", None), ("strict", [3, 11])])
 def test_backward_matches_finite_differences(causal, kv_lens):
     """N=16, d=4, central differences with h = 1e-6 on L = sum(dO * O)."""
     B, H, N, d = 2, 1, 16, 4
@@ -37,7 +38,7 @@ def test_backward_matches_finite_differences(causal, kv_lens):
             fd[idx] = (lp - lm) / (2 * h)
         err = np.abs(fd - g) / np.maximum(1.0, np.abs(g))
         assert np.max(err) < 1e-7, (name, np.max(err))
-    if kv_lens is not None:
+    if kv_lens is not None and kv_lens[0] == 0:
         # A batch with no visible key has zero gradients everywhere.
         assert np.all(dq[0] == 0) and np.all(dk[0] == 0) and np.all(dv[0] == 0)
 

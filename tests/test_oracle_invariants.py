@@ -25,7 +25,10 @@ def _brute(q, k, v, scale, causal, kv_lens):
         kvl = N if kv_lens is None else int(kv_lens[b])
         for h in range(H):
             for i in range(N):
-                keys = [j for j in range(N) if j < kvl and (not causal or j <= i)]
+                if causal == "strict":
+                    keys = [j for j in range(N) if j < kvl and j < i]
+                else:
+                    keys = [j for j in range(N) if j < kvl and (not causal or j <= i)]
                 if not keys:
                     o[b, h, i] = 0.0
                     lse[b, h, i] = -INF
@@ -45,7 +48,7 @@ def _brute(q, k, v, scale, causal, kv_lens):
     return o, lse
 
 
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, "strict"])
 @pytest.mark.parametrize("kv_lens", [None, [0, 1, 5, 8]])
 def test_naive_matches_brute_force(causal, kv_lens):
     B, H, N, d = 4, 2, 8, 4
@@ -200,3 +203,36 @@ def test_page_examples_through_qkv(golden):
     # Cell D2 through key padding: no visible key at all.
     o, lse = orc.attn_fwd_naive(q, k, v, 1.0, causal=True, kv_lens=[0])
     assert np.all(o == 0.0) and np.all(lse == -INF)
+
+
+def test_strict_causal_first_row_is_the_guard():
+    # "Worked examples", Cell D2: with the strict mask the first query sees no
+    # key at all, and the guard returns O = 0, lse = -inf.
+    q, k, v = _rand((2, 3, 9, 5), 31), _rand((2, 3, 9, 5), 32), _rand((2, 3, 9, 5), 33)
+    o, lse = orc.attn_fwd_naive(q, k, v, 0.4, "strict")
+    assert np.all(o[:, :, 0] == 0.0) and np.all(lse[:, :, 0] == -INF)
+    assert np.all(np.isfinite(lse[:, :, 1:]))
+    # Row 1 sees key 0 only: O = V_0, lse = its score.
+    assert np.max(np.abs(o[:, :, 1] - v[:, :, 0])) < 1e-15
+    s10 = 0.4 * np.sum(q[:, :, 1] * k[:, :, 0], axis=-1)
+    assert np.max(np.abs(lse[:, :, 1] - s10)) < 1e-14
+
+
+@pytest.mark.parametrize("kv_lens", [None, [7, 3]])
+def test_strict_causal_is_causal_shifted_by_one(kv_lens):
+    # Query i under j < i is query i placed at position i-1 under j <= i-1:
+    # drop the first query and the last key/value.
+    B, H, N, d = 2, 2, 12, 4
+    q, k, v = _rand((B, H, N, d), 41), _rand((B, H, N, d), 42), _rand((B, H, N, d), 43)
+    o, lse = orc.attn_fwd_naive(q, k, v, 0.7, "strict", kv_lens)
+    kv2 = None if kv_lens is None else [min(x, N - 1) for x in kv_lens]
+    o2, lse2 = orc.attn_fwd_naive(q[:, :, 1:], k[:, :, :-1], v[:, :, :-1], 0.7, True, kv2)
+    assert np.max(np.abs(o[:, :, 1:] - o2)) < 1e-13
+    fin = np.isfinite(lse2)
+    assert np.array_equal(fin, np.isfinite(lse[:, :, 1:]))
+    assert np.max(np.abs(lse[:, :, 1:][fin] - lse2[fin])) < 1e-13
+
+
+def test_unknown_mask_is_rejected():
+    with pytest.raises(ValueError):
+        orc.visible(4, 4, "diagonal", 4)
