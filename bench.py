@@ -7,7 +7,10 @@ Q/K/V iid N(0,1) from a seeded CPU generator, already resident in device
 memory when timing starts. A timed step is one fa_fwd launch over the whole
 batch (value = forward TFLOP/s at 4*B*H*N^2*d/2 FLOPs). The backward pass is
 timed the same way and reported beside it ("bwd"), together with one full
-forward+backward pass ("fwd_bwd_step").
+forward+backward pass ("fwd_bwd_step"), fa_fwd_split is compared with
+fa_fwd on a grid too small to fill the GPU ("split_kv"), and a naive forward
+that materialises S and P in device memory (PyTorch matmul + softmax, the
+comparison path, not part of libfa) is timed on the same inputs ("naive").
 
 Prints ONE JSON line. Timing uses HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
@@ -29,6 +32,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2h16n4096d128_traffic.json")
+SWEEP_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_bh32d128_traffic_sweep.json")
+SWEEP_N = (1024, 2048, 4096, 8192, 16384)  # causal, B=2, H=16, d=128
 KERNEL_SOURCES = [
     os.path.join(ROOT, "exact_io_aware_17_amd", "csrc", f)
     for f in ("fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h")
@@ -97,8 +102,10 @@ COPY_BYTES = 256 * 2 ** 20  # calibration copy: 256 MiB read + 256 MiB written
 
 
 def profile_run(w) -> int:
-    """A short run for counter collection: a plain copy of known size, then the
-    forward kernel, three times each."""
+    """A short run for counter collection: a plain copy of known size three
+    times, the forward kernel on the workload three times, then once at each
+    N of the traffic sweep (causal, B=2, H=16, d=128), then the naive
+    forward once on the workload."""
     import torch
     import exact_io_aware_17_amd as fa
     from exact_io_aware_17_amd import workloads as W
@@ -116,7 +123,18 @@ def profile_run(w) -> int:
     for _ in range(3):
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kv)
     torch.cuda.synchronize()
-    print("profile run done", flush=True)
+    print("profile run: workload done", flush=True)
+    for n in SWEEP_N:
+        ws = W.with_shape(W.BY_ID[5], N=n)
+        xs = W.make_inputs(ws)
+        qs, ks, vs = (xs[c].to(dev) for c in ("q", "k", "v"))
+        fa.fwd(qs, ks, vs, causal=True, scale=ws.scale)
+        torch.cuda.synchronize()
+        del qs, ks, vs
+        print(f"profile run: sweep N={n} done", flush=True)
+    naive_forward(q, k, v, w.scale, w.causal)
+    torch.cuda.synchronize()
+    print("profile run: naive forward done", flush=True)
     return 0
 
 
@@ -126,33 +144,119 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
     import csv
     import glob
 
+    from exact_io_aware_17_amd import workloads as W
+
     def read(d, counter):
-        rows = []
+        rows = []  # (dispatch id, kernel name, value in KiB), dispatch order
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] == counter:
-                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-        return rows
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 float(r["Counter_Value"])))
+        return sorted(rows)
 
     out = {"kernel_source_hash": kernel_source_hash(), "command": command,
            "copy_bytes": COPY_BYTES}
+    sweep = {"kernel_source_hash": out["kernel_source_hash"], "command": command,
+             "shape": "causal, B=2, H=16, d=128, bf16", "rows": []}
+    per_key = {}
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         rows = read(d, counter)
-        copy = [v for n, v in rows if "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
-        fwd = [v for n, v in rows if "fwd_bf16" in n]
-        if not copy or not fwd:
-            print(f"no {counter} readings for the copy or the forward kernel", file=sys.stderr)
+        copy = [v for _, n, v in rows if "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
+        fwd = [v for _, n, v in rows if "fwd_bf16" in n]
+        if not copy or len(fwd) != 3 + len(SWEEP_N):
+            print(f"{counter}: expected copy readings and {3 + len(SWEEP_N)} forward "
+                  f"dispatches, got {len(copy)} and {len(fwd)}", file=sys.stderr)
             return 1
         scale = COPY_BYTES / (sorted(copy)[len(copy) // 2] * 1024.0)
-        per_launch = sorted(fwd)[len(fwd) // 2] * 1024.0 * scale
-        out[key + "_kib_raw"] = sorted(fwd)[len(fwd) // 2]
+        last_fwd = max(i for i, n, _ in rows if "fwd_bf16" in n)
+        naive = sum(v for i, _, v in rows if i > last_fwd) * 1024.0 * scale
+        out["naive_" + key + "_bytes"] = naive
+        wl = sorted(fwd[:3])[1]
+        out[key + "_kib_raw"] = wl
         out[key + "_scale"] = scale
-        out[key + "_bytes_per_launch"] = per_launch
+        out[key + "_bytes_per_launch"] = wl * 1024.0 * scale
+        per_key[key] = [v * 1024.0 * scale for v in fwd[3:]]
     out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    out["naive_hbm_bytes"] = out["naive_fetch_bytes"] + out["naive_write_bytes"]
+    out["naive_over_fa_fwd"] = out["naive_hbm_bytes"] / out["hbm_bytes_per_launch"]
+    for i, n in enumerate(SWEEP_N):
+        alg = W.fwd_bytes(2, 16, n, 128, 2)
+        meas = per_key["fetch"][i] + per_key["write"][i]
+        sweep["rows"].append({"N": n, "fetch_bytes": per_key["fetch"][i],
+                              "write_bytes": per_key["write"][i], "hbm_bytes": meas,
+                              "algorithmic_bytes": alg, "ratio": meas / alg,
+                              "s_p_roundtrip_bytes": 2 * 2 * 16 * W.score_matrix_bytes(n, 2)})
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    with open(SWEEP_FILE, "w") as f:
+        json.dump(sweep, f, indent=1)
     print(json.dumps(out))
+    print(json.dumps(sweep))
     return 0
+
+
+def naive_forward(q, k, v, scale, causal):
+    """The unfused path the pages contrast with: S = scale Q K^T and
+    P = softmax(S) written to and read back from device memory (bf16), then
+    O = P V. A comparison baseline only."""
+    import torch
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        n = q.shape[-2]
+        hidden = torch.ones(n, n, dtype=torch.bool, device=q.device).triu_(1)
+        s = s.masked_fill(hidden, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    return torch.matmul(p, v)
+
+
+def naive_comparison(w, q, k, v, o, stream, reps=5):
+    import torch
+    from exact_io_aware_17_amd import workloads as W
+
+    for _ in range(2):
+        on = naive_forward(q, k, v, w.scale, w.causal)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        on = naive_forward(q, k, v, w.scale, w.causal)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = W.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    diff = (on.float() - o.float()).abs()
+    return {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "what": "torch bf16 matmul + scale + mask + softmax + matmul (S, P in HBM)",
+            "max_abs_diff_vs_fa_fwd": round(float(diff.max().item()), 5)}
+
+
+def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
+    """fa_fwd vs fa_fwd_split on a causal grid too small to fill the GPU."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    from exact_io_aware_17_amd import workloads as W
+
+    g = torch.Generator().manual_seed(17099)
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+    res = {"shape": f"causal B={B} H={H} N={N} d={d}",
+           "workspace_bytes": fa.split_workspace_bytes(B, H, N, d, True)}
+    flops = W.fwd_flops(B, H, N, d, True)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    for name, split in (("fa_fwd", False), ("fa_fwd_split", True)):
+        for _ in range(3):
+            fa.fwd(q, k, v, causal=True, split=split)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fa.fwd(q, k, v, causal=True, split=split)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[name] = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    return res
 
 
 def main() -> int:
@@ -251,7 +355,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128,32,2,causal>",
+            "kernel": "fwd_bf16_kernel<128, 32, 2, true>",
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_kernel, 5),
             "kernel_ms_min": round(per_launch[0], 5),
@@ -288,6 +392,11 @@ def main() -> int:
                       "flop_convention": "10*B*H*N^2*d, halved for causal"}
         out["fwd_bwd_step"] = {"ms": round(ms_fb, 5),
                                "tflops": round((flops + bflops) / (ms_fb * 1e-3) / 1e12, 2)}
+
+    if not args.no_bwd:
+        out["split_kv"] = split_kv_comparison(dev, stream)
+        out["naive"] = naive_comparison(w, q, k, v, o, stream)
+        out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w)

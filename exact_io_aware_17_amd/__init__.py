@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     FA_ERR_INVALID_ARG,
     FA_ERR_UNSUPPORTED,
     FA_MASK_CAUSAL,
+    FA_MASK_CAUSAL_STRICT,
     FA_MASK_NONE,
     FA_OK,
     FaError,
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     default_scale,
     fwd,
     load,
+    mask_kind,
     schedule,
     split_workspace_bytes,
     status_string,

@@ -20,6 +20,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
+FA_MASK_CAUSAL_STRICT = 2
 ABI_VERSION = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -92,6 +93,16 @@ def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def mask_kind(causal) -> int:
+    """causal: False (no mask), True (key j visible to query i iff j <= i) or
+    "strict" (iff j < i)."""
+    if isinstance(causal, str):
+        if causal != "strict":
+            raise ValueError("causal must be False, True or 'strict'")
+        return FA_MASK_CAUSAL_STRICT
+    return FA_MASK_CAUSAL if causal else FA_MASK_NONE
+
+
 def default_scale(d: int) -> float:
     """float32(1/sqrt(d)), the value every path receives."""
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
@@ -131,14 +142,14 @@ _FWD_WS = {}
 _FWD_WS_BYTES = {}
 
 
-def split_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+def split_workspace_bytes(B: int, H: int, N: int, d: int, causal=False) -> int:
     """fa_fwd_split_workspace_bytes for the current device (memoised per shape)."""
     key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, B, H, N, d,
-           bool(causal))
+           mask_kind(causal))
     n = _FWD_WS_BYTES.get(key)
     if n is None:
         n = int(load().fa_fwd_split_workspace_bytes(B, H, N, d,
-                                                    FA_MASK_CAUSAL if causal else FA_MASK_NONE))
+                                                    mask_kind(causal)))
         _FWD_WS_BYTES[key] = n
     return n
 
@@ -152,19 +163,19 @@ def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def schedule(N: int, BH: int, causal: bool, cus: int, occ: int):
+def schedule(N: int, BH: int, causal, cus: int, occ: int):
     """fa_fwd_schedule: (items, nslots) of fa_fwd_split's work plan (host only)."""
     lib = load()
     buf = (ctypes.c_uint32 * 4096)()
     ns = ctypes.c_int(0)
-    n = lib.fa_fwd_schedule(N, BH, FA_MASK_CAUSAL if causal else FA_MASK_NONE, cus, occ, buf,
+    n = lib.fa_fwd_schedule(N, BH, mask_kind(causal), cus, occ, buf,
                             4096, ctypes.byref(ns))
     if n < 0:
         raise FaError("fa_fwd_schedule", n, status_string(n))
     return [int(buf[i]) for i in range(n)], int(ns.value)
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
         scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         split: bool = False, workspace: Optional[torch.Tensor] = None
@@ -198,7 +209,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     kvp = _kv_ptr(kv_lens, B, q.device)
     lib = load()
-    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    mask = mask_kind(causal)
     with torch.cuda.device(q.device):
         if fn_name == "fa_fwd_f32":
             st = lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
@@ -229,7 +240,7 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-        lse: torch.Tensor, dout: torch.Tensor, causal: bool = False,
+        lse: torch.Tensor, dout: torch.Tensor, causal=False,
         scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
@@ -258,6 +269,6 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     with torch.cuda.device(q.device):
         st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, float(scale),
-                        FA_MASK_CAUSAL if causal else FA_MASK_NONE, kvp, _stream(q.device))
+                        mask_kind(causal), kvp, _stream(q.device))
     _check("fa_bwd", st)
     return dq, dk, dv

@@ -22,7 +22,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_common(int B, int H, int N, int d, float scale, int mask_kind) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
+      mask_kind != FA_MASK_CAUSAL_STRICT)
+    return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   // Row indices (b*H + h)*N + i are formed in 32-bit arithmetic.
   if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
@@ -82,7 +84,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.d = d;
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
-  p.causal = (mask_kind == FA_MASK_CAUSAL);
+  p.causal = (mask_kind != FA_MASK_NONE);
+  p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
   p.nslots = 0;
   p.counters = nullptr;
   p.part_ml = nullptr;
@@ -139,7 +142,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int mask_kind) {
   if (check_common(B, H, N, d, 1.f, mask_kind) != FA_OK) return 0;
-  const bool causal = (mask_kind == FA_MASK_CAUSAL);
+  const bool causal = (mask_kind != FA_MASK_NONE);
   int cus = 0, occ = 0;
   fa::fwd_occupancy(d, causal, &cus, &occ);
   const fa::FwdPlan& plan = fa::fwd_plan(N, B * H, causal, cus, occ);
@@ -163,8 +166,10 @@ int fa_fwd_schedule(int N, int BH, int mask_kind, int cus, int occ, uint32_t* it
                     int max_items, int* nslots) {
   if (N <= 0 || BH <= 0 || cus < 0 || occ < 0 || max_items < 0 || (max_items > 0 && !items))
     return FA_ERR_INVALID_ARG;
-  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
-  const fa::FwdPlan& plan = fa::fwd_plan(N, BH, mask_kind == FA_MASK_CAUSAL, cus, occ);
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
+      mask_kind != FA_MASK_CAUSAL_STRICT)
+    return FA_ERR_INVALID_ARG;
+  const fa::FwdPlan& plan = fa::fwd_plan(N, BH, mask_kind != FA_MASK_NONE, cus, occ);
   for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
   if (nslots) *nslots = plan.nslots;
   return plan.nitems;
@@ -219,7 +224,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.d = d;
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
-  p.causal = (mask_kind == FA_MASK_CAUSAL);
+  p.causal = (mask_kind != FA_MASK_NONE);
+  p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
   hipError_t e = fa::launch_bwd_bf16(p, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

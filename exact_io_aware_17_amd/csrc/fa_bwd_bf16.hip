@@ -197,6 +197,7 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
   const __bf16* dO = (const __bf16*)p.dout + head;
 
   const int qa = q0 + wave * 32;
+  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
   const int qrow = qa + n;
   const int qrow_c = min(qrow, N - 1);
   bf16x8 qf[DC], of[DC];
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
     __syncthreads();
     issue(j + 1);
     const int key0 = j * BS;
-    if (CAUSAL && key0 > qa + 31) continue;  // wholly in this wave's future
+    if (CAUSAL && key0 + dg > qa + 31) continue;  // wholly in this wave's future
     const char* ks = kbuf[j & 1];
     const char* vs = vbuf[j & 1];
 
@@ -240,9 +241,9 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
       dp = mfma32(*(const bf16x8*)(vs + off.roff[c]), of[c], dp);
     }
     __builtin_amdgcn_s_setprio(0);
-    const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa);
+    const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 + dg > qa);
     int lim = kvlen - 1;  // key visible iff key <= lim
-    if (CAUSAL) lim = min(lim, qrow);
+    if (CAUSAL) lim = min(lim, qrow - dg);
     lim -= key0 + 4 * h;
     bf16x8 df[2];
 #pragma unroll
@@ -302,6 +303,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
   const float* deltag = p.delta + (size_t)bh * N;
 
   const int kw0 = kb0 + wave * 32;
+  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
   const int key = kw0 + n;
   const int key_c = min(key, N - 1);
   bf16x8 kf[DC], vf[DC];
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
     issue(i + 1);
     const int qb0 = i * BS;
     if (kw0 >= kvlen) continue;                  // all of this wave's keys are hidden
-    if (CAUSAL && kw0 > qb0 + BS - 1) continue;  // every query of the block precedes them
+    if (CAUSAL && kw0 + dg > qb0 + BS - 1) continue;  // every query of the block precedes them
     const char* qs = qbuf[i & 1];
     const char* os = obuf[i & 1];
     const float* st = stat[i & 1];
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
 #pragma unroll
     for (int c = 0; c < DC; ++c) s = mfma32(*(const bf16x8*)(qs + off.roff[c]), kf[c], s);
     __builtin_amdgcn_s_setprio(0);
-    const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0);
+    const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 + dg > qb0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int ql = 8 * g + 4 * h;  // four consecutive queries of this lane
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
         float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[e]));
         if (need_mask) {
           const int query = qb0 + ql + e;
-          if (key >= kvlen || query >= N || (CAUSAL && key > query)) pr = 0.f;
+          if (key >= kvlen || query >= N || (CAUSAL && key + dg > query)) pr = 0.f;
         }
         s[r] = pr;  // P, fp32
       }

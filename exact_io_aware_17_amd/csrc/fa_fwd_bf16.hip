@@ -168,6 +168,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   const int jend = min((part + 1) * nbn / nparts, nblk);
   const int qa = q0 + wave * 32;  // first query of this wave
   const int qrow = qa + n;
+  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
 
   const size_t head = (size_t)bh * N * D;
   const __bf16* __restrict__ Q = (const __bf16*)p.q + head;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
     const int key0 = j * BN;
     // Skip blocks wholly in this wave's future (all its rows would be masked).
-    if (CAUSAL && key0 > qa + 31) return;
+    if (CAUSAL && key0 + dg > qa + 31) return;
     const char* ks = kbuf[ST];
     const char* vs = vbuf[ST];
 
@@ -282,10 +283,10 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
     __builtin_amdgcn_s_setprio(0);
     // ---- a3: mask (only blocks that straddle the diagonal or kv_len) ----
-    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa);
+    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 + dg > qa);
     if (need_mask) {
       int lim = kvlen - 1;  // key visible iff key <= lim
-      if (CAUSAL) lim = min(lim, qrow);
+      if (CAUSAL) lim = min(lim, qrow - dg);
       lim -= key0 + 4 * h;
 #pragma unroll
       for (int t = 0; t < KT; ++t)

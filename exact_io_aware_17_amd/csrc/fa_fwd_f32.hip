@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       for (int t = 0; t < HD; ++t) dot = fmaf(q[t], ks[jj][half * HD + t], dot);
       dot += __shfl_xor(dot, 1);
       const int key = key0 + jj;
-      const bool vis = (key < kvlen) && (!CAUSAL || key <= qrow);
+      const bool vis = (key < kvlen) && (!CAUSAL || key + p.diag <= qrow);
       const float s = vis ? dot * scale : NEG_INF;
       sc[jj] = s;
       bmax = fmaxf(bmax, s);

@@ -17,7 +17,8 @@ struct FwdParams {
   int B, H, N, d;
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
-  int causal;
+  int causal;              // key j visible to query i only if j <= i - diag
+  int diag;                // 0: causal (j <= i), 1: strict causal (j < i)
   // Split work items (used only with a plan of nitems > 0): per (b, h)
   // nslots partial states, each BM rows of unnormalised O (fp32) plus the
   // row max and both row sums, and one arrival counter per query tile.
@@ -79,6 +80,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   int causal;
+  int diag;                // as FwdParams
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().

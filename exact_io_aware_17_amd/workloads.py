@@ -30,7 +30,7 @@ class Workload:
     N: int
     d: int
     dtype: str              # "f32" or "bf16"
-    causal: bool
+    causal: object  # False, True (key j visible iff j <= i) or "strict" (iff j < i)
     q_mult: float = 1.0     # Q is multiplied by this before the cast
     padded: bool = False    # per-batch key lengths are drawn
     backward: bool = False  # an upstream gradient dO is drawn too

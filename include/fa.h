@@ -16,7 +16,8 @@
  * examples", Cell D2, the guard).
  *
  * Visibility: key j is visible to query i iff
- *   (mask_kind != FA_MASK_CAUSAL || j <= i)  &&  j < kv_len_b,
+ *   (mask_kind != FA_MASK_CAUSAL || j <= i)  &&
+ *   (mask_kind != FA_MASK_CAUSAL_STRICT || j < i)  &&  j < kv_len_b,
  * where kv_len_b = kv_lens[b] clamped to [0, N] (kv_lens == NULL means N).
  * Causal masking is top-left aligned (queries and keys share positions
  * 0..N-1). Padding hides keys only; every query row is computed.
@@ -61,8 +62,11 @@ typedef enum {
 } fa_status;
 
 typedef enum {
-  FA_MASK_NONE = 0,   /* every key visible (subject to kv_lens) */
-  FA_MASK_CAUSAL = 1  /* key j visible to query i iff j <= i */
+  FA_MASK_NONE = 0,          /* every key visible (subject to kv_lens) */
+  FA_MASK_CAUSAL = 1,        /* key j visible to query i iff j <= i */
+  FA_MASK_CAUSAL_STRICT = 2  /* key j visible to query i iff j < i: the variant
+                                of "Worked examples", Cell D2, whose first row
+                                sees no key (O = 0, lse = -inf) */
 } fa_mask_kind;
 
 /*

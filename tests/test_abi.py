@@ -68,7 +68,8 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, scale=float("inf")) == INV
     assert _fwd(fn, scale=0.0) == INV
     assert _fwd(fn, scale=-0.125) == INV
-    assert _fwd(fn, mask=2) == INV
+    assert _fwd(fn, mask=3) == INV
+    assert _fwd(fn, mask=-1) == INV
     assert _fwd(fn, o=A + 8) == INV                 # output overlaps q
     assert _fwd(fn, lse=A + SZ + 64) == INV         # lse overlaps k
     assert _fwd(fn, d=96) == UNS

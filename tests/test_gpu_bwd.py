@@ -40,7 +40,7 @@ def test_workload5_backward_full():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("causal", [False, True, "strict"])
 @pytest.mark.parametrize("N", [1, 100, 257])
 def test_backward_ragged(d, causal, N):
     w = W.Workload(95, "bwd ragged", 2, 2, N, d, "bf16", causal, backward=True)

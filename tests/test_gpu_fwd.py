@@ -111,6 +111,23 @@ def test_key_padding_with_empty_and_single_rows(dtype, causal):
     assert torch.equal(o[1], v[1, :, :1, :].expand_as(o[1]))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 77, 333])
+def test_strict_causal(dtype, d, N):
+    w = W.Workload(97, f"strict N={N}", 2, 3, N, d, dtype, "strict")
+    x, o, lse = _full_check(w)
+    # "Worked examples", Cell D2 through the strict mask: row 0 sees no key.
+    assert torch.all(o[:, :, 0] == 0) and torch.all(torch.isneginf(lse[:, :, 0]))
+    if N > 1:  # row 1 sees key 0 only
+        assert torch.equal(o[:, :, 1], x["v"].to(DEV)[:, :, 0])
+
+
+def test_strict_causal_with_padding():
+    w = W.Workload(98, "strict padded", 3, 2, 300, 128, "bf16", "strict")
+    _full_check(w, kv_lens=torch.tensor([0, 1, 170], dtype=torch.int32))
+
+
 def test_kv_lens_out_of_range_are_clamped():
     w = W.Workload(92, "clamp", 3, 1, 130, 64, "bf16", False)
     x = W.make_inputs(w)

@@ -27,6 +27,7 @@ CASES = [
     (2, 2, 640, 64, False, [0, 333]),     # an empty batch and parts beyond kv_len
     (1, 2, 4096, 128, True, None),
     (2, 1, 2048, 128, True, [2048, 700]),
+    (1, 2, 2048, 128, "strict", None),    # row 0 of every head sees no key
 ]
 
 
@@ -38,7 +39,8 @@ def _inputs(B, H, N, d, seed):
 
 def _ids(c):
     B, H, N, d, causal, kv = c
-    return f"B{B}H{H}N{N}d{d}{'c' if causal else ''}{'' if kv is None else 'kv'}"
+    tag = {False: "", True: "c", "strict": "s"}[causal]
+    return f"B{B}H{H}N{N}d{d}{tag}{'' if kv is None else 'kv'}"
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
