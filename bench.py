@@ -162,7 +162,9 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
     per_key = {}
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         rows = read(d, counter)
-        copy = [v for _, n, v in rows if "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
+        first_fwd = min((i for i, n, _ in rows if "fwd_bf16" in n), default=-1)
+        copy = [v for i, n, v in rows
+                if i < first_fwd and "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
         fwd = [v for _, n, v in rows if "fwd_bf16" in n]
         if not copy or len(fwd) != 3 + len(SWEEP_N):
             print(f"{counter}: expected copy readings and {3 + len(SWEEP_N)} forward "
@@ -267,6 +269,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-split-kv", action="store_true",
+                    help="skip the fa_fwd_split comparison (it launches the forward kernel "
+                         "at another shape)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run (copy calibration + forward) for rocprofv3 counters")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -394,7 +399,8 @@ def main() -> int:
                                "tflops": round((flops + bflops) / (ms_fb * 1e-3) / 1e12, 2)}
 
     if not args.no_bwd:
-        out["split_kv"] = split_kv_comparison(dev, stream)
+        if not args.no_split_kv:
+            out["split_kv"] = split_kv_comparison(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
 

@@ -67,7 +67,7 @@ __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 
 __device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
 __device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
 
-// ---- a7 (and the lse preparation): per row D_i and lse_i * log2(e) ----
+// ---- per row: D_i = sum_c dO_ic O_ic and lse_i * log2(e) ----
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each

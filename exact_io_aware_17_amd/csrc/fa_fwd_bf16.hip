@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   const int n = lane & 31;  // query of this lane within the wave / row within an MFMA tile
   const int h = lane >> 5;  // lane half
 
-  // ---- a0: work item ----
+  // ---- work item ----
   const int N = p.N;
   const int ntiles = (N + BM - 1) / BM;
   // Item-major order: workgroup id w takes item w / (B*H) of head w % (B*H).
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- a1: K/V block stream, HBM -> LDS ----
+  // ---- K/V block stream, HBM -> LDS ----
   // Per-lane source offsets inside a block (bytes), fixed for the kernel: a
   // block's DMA then needs only a scalar base. A block that runs past row
   // N-1 (the ragged end) takes the clamped path.
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     const char* ks = kbuf[ST];
     const char* vs = vbuf[ST];
 
-    // ---- a2: S^T = K Q^T for BN keys x 32 queries ----
+    // ---- S^T = K Q^T for BN keys x 32 queries ----
     // Waves in a matrix phase get issue priority over waves in their softmax,
     // so whichever wave has MFMAs ready keeps the matrix pipe fed while the
     // others' VALU work fills the gaps.
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
         s[t] = mfma32(*(const bf16x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
 
     __builtin_amdgcn_s_setprio(0);
-    // ---- a3: mask (only blocks that straddle the diagonal or kv_len) ----
+    // ---- mask (only blocks that straddle the diagonal or kv_len) ----
     const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 + dg > qa);
     if (need_mask) {
       int lim = kvlen - 1;  // key visible iff key <= lim
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
           if (t * 32 + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = NEG_INF;
     }
 
-    // ---- a4: online softmax ----
+    // ---- online softmax ----
     // Probabilities against the current reference max m_run. While the
     // block's row max stays within TAU of it every p is at most 2^TAU, so a
     // lane sum above 2^TAU (or not a number: m_run = -inf at the start) is
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     l_bf += lbf_blk;
 
     __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
-    // ---- a5: O^T += V^T P^T ----
+    // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     l_bf = lbf_sum;
   }
 
-  // ---- a6: finalize ----
+  // ---- finalize ----
   const float l_tot = pair_sum(l_run);
   const float l_o = pair_sum(l_bf);
   const bool empty = (l_tot == 0.f);
