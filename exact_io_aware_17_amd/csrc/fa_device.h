@@ -22,19 +22,26 @@ constexpr float POS_INF = __builtin_huge_valf();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 
-// Physical 16-byte slot of logical chunk c in a row-major tile row of D bf16
-// (D*2 bytes). The XOR spreads 16 consecutive rows over 16 distinct slots.
+// Forward K/V tiles (rows of D bf16). K rows are read whole (16 consecutive
+// rows at one chunk): chunk c of row `row` is stored at slot c ^ kswz(row).
+// V rows are read transposed (8 consecutive rows x 4 chunks at a time):
+// slot c ^ vswz(row).
 template <int D>
-__device__ __forceinline__ int row_slot(int row, int c) {
+__device__ __forceinline__ int kswz(int row) {
   if constexpr (D == 128) {
-    return c ^ (row & 15);
+    return row & 15;
   } else {
-    return c ^ ((row >> 1) & 7);
+    return (row >> 1) & 7;
   }
 }
-
-// Physical slot of logical chunk c in a transposed tile row of 64 bf16 (128 B).
-__device__ __forceinline__ int t64_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) {
+    return 4 * (row & 3);
+  } else {
+    return 4 * ((row >> 1) & 1);
+  }
+}
 
 // Position of index x inside its 16-group of a transposed tile: bits 2 and 3
 // swapped. This is the order in which a 32x32 MFMA accumulator holds the

@@ -87,26 +87,6 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 #define FA_FWD_WG_PER_CU 3
 #endif
 
-// K rows: 16-byte chunk c of row `row` is stored at slot c ^ kswz(row).
-template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  if constexpr (D == 128) {
-    return row & 15;
-  } else {
-    return (row >> 1) & 7;
-  }
-}
-
-// V rows: the transpose reads touch 8 consecutive rows x 4 chunks at a time.
-template <int D>
-__device__ __forceinline__ int vswz(int row) {
-  if constexpr (D == 128) {
-    return 4 * (row & 3);
-  } else {
-    return 4 * ((row >> 1) & 1);
-  }
-}
-
 template <int D, int BN, int STAGES, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p, FwdPlan plan) {
   constexpr int ROWB = D * 2;                 // bytes per K/V row
