@@ -21,9 +21,15 @@ What is computed (sources are the five pages on exact, IO-aware attention):
 Readings taken where the pages leave a step open (each is listed with the
 design notes of this repository):
 
-* causal means key j is visible to query i iff j <= i (top-left aligned,
-  N_q = N_k); the strict variant (j < i), which the pages use in Cell D2 to
-  produce a row with no visible key, is selected with causal="strict";
+* causal means key j is visible to query i iff j <= i + (N_k - N_q): with
+  N_q = N_k that is j <= i, and with fewer queries than keys the queries are
+  the last N_q positions (bottom-right alignment, as when new queries attend
+  to a longer cache); the strict variant (j < i + (N_k - N_q)), which the
+  pages use in Cell D2 to produce a row with no visible key, is selected with
+  causal="strict";
+* grouped heads: K and V may have H_kv heads, a divisor of the H query
+  heads; query head h reads K/V head h // (H / H_kv) (H_kv = H is the
+  pages' per-head attention, H_kv = 1 a single shared K/V head);
 * key padding kv_lens[b] hides keys j >= kv_lens[b] for every query of batch
   b; queries are never dropped;
 * the merge of two states whose maxima are both -inf keeps the empty state
@@ -189,18 +195,20 @@ def visible(n_rows: int, n_keys: int, causal, kv_len: int,
             rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Boolean [len(rows), n_keys]: key j visible to query i.
 
-    causal is False (no mask), True (j <= i) or "strict" (j < i). Visible iff
-    the causal condition holds and j < kv_len. Causal masking follows "Worked
-    examples", Cell D (keys in the query's future are hidden); the strict
-    form, which also hides the query's own position, is the variant of Cell
-    D2; the key-padding length is this repository's reading for batched,
-    padded inputs (keys only are padded).
+    causal is False (no mask), True (j <= i + off) or "strict"
+    (j < i + off), with off = n_keys - n_rows: query i sits at key position
+    i + off (bottom-right alignment; off = 0 when there are as many queries
+    as keys). Visible iff the causal condition holds and j < kv_len. Causal
+    masking follows "Worked examples", Cell D (keys in the query's future
+    are hidden); the strict form, which also hides the query's own position,
+    is the variant of Cell D2; the key-padding length is this repository's
+    reading for batched, padded inputs (keys only are padded).
     """
     if causal not in (False, True, "strict"):
         raise ValueError("causal must be False, True or 'strict'")
     if rows is None:
         rows = np.arange(n_rows)
-    i = np.asarray(rows)[:, None]
+    i = np.asarray(rows)[:, None] + (n_keys - n_rows)
     j = np.arange(n_keys)[None, :]
     vis = j < kv_len
     if causal == "strict":
@@ -208,6 +216,13 @@ def visible(n_rows: int, n_keys: int, causal, kv_len: int,
     elif causal:
         vis = vis & (j <= i)
     return vis
+
+
+def _kv_head(h: int, H: int, Hkv: int) -> int:
+    """K/V head read by query head h when K and V have Hkv of the H heads."""
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("the number of K/V heads must divide the number of query heads")
+    return h // (H // Hkv)
 
 
 def _kv_len(kv_lens, b: int, n: int) -> int:
@@ -221,10 +236,12 @@ def attn_fwd_naive(q, k, v, scale: float, causal: bool = False, kv_lens=None,
                    heads: Optional[Sequence[Tuple[int, int]]] = None):
     """Standard attention by its definition, with the full score matrix.
 
-    q, k, v: [B, H, N, d] (any float dtype; upcast to float64 losslessly).
+    q: [B, H, N, d]; k, v: [B, H_kv, N_k, d] with H_kv dividing H (any float
+    dtype; upcast to float64 losslessly).
     scale: the caller's scale (tests pass the float32 value the GPU receives).
-    causal: False, True (hide keys j > i) or "strict" (hide keys j >= i).
-    kv_lens: None or per-batch valid key counts.
+    causal: False, True or "strict" (see ``visible``: bottom-right aligned
+    when N_k != N).
+    kv_lens: None or per-batch valid key counts (clamped to [0, N_k]).
     rows: optional query indices to compute (rows are independent, so this is
     the same definition restricted to those rows).
     heads: optional list of (b, h) to compute; others are left as NaN.
@@ -238,7 +255,7 @@ def attn_fwd_naive(q, k, v, scale: float, causal: bool = False, kv_lens=None,
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     alpha = float(scale)
     row_idx = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_idx.shape[0]
@@ -248,15 +265,16 @@ def attn_fwd_naive(q, k, v, scale: float, causal: bool = False, kv_lens=None,
     todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in todo:
         kvl = _kv_len(kv_lens, b, Nk)
+        hk = _kv_head(h, H, Hkv)
         vis = visible(N, Nk, causal, kvl, row_idx)
-        s = alpha * (q[b, h, row_idx] @ k[b, h].T)
+        s = alpha * (q[b, h, row_idx] @ k[b, hk].T)
         s = np.where(vis, s, NEG_INF)
         m = np.max(s, axis=1)
         empty = m == NEG_INF
         m_safe = np.where(empty, 0.0, m)
         p = np.exp(s - m_safe[:, None])          # exp(-inf) = 0 on hidden keys
         l = np.sum(p, axis=1)
-        num = p @ v[b, h]
+        num = p @ v[b, hk]
         with np.errstate(invalid="ignore", divide="ignore"):
             o = num / l[:, None]
             lse = m + np.log(l)
@@ -279,18 +297,19 @@ def attn_fwd_tiled(q, k, v, scale: float, causal: bool = False, kv_lens=None,
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     alpha = float(scale)
     o_out = np.zeros((B, H, N, v.shape[3]))
     lse_out = np.zeros((B, H, N))
     for b in range(B):
         kvl = _kv_len(kv_lens, b, Nk)
         for h in range(H):
+            hk = _kv_head(h, H, Hkv)
             vis = visible(N, Nk, causal, kvl)
-            s_all = alpha * (q[b, h] @ k[b, h].T)
+            s_all = alpha * (q[b, h] @ k[b, hk].T)
             s_all = np.where(vis, s_all, NEG_INF)
             for i in range(N):
-                o, _, _, lse = online_row(s_all[i], v[b, h], block, order, rescale)
+                o, _, _, lse = online_row(s_all[i], v[b, hk], block, order, rescale)
                 o_out[b, h, i] = o
                 lse_out[b, h, i] = lse
     return o_out, lse_out
@@ -309,11 +328,13 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool = False, kv_lens=None):
         dS   = P * (dP - D)
         dQ   = scale * dS K
         dK   = scale * dS^T Q
+    With grouped K/V heads (H_kv < H), dK and dV of a K/V head sum the
+    contributions of every query head that reads it.
     O and lse come from this module's own forward. Returns (dq, dk, dv) float64.
     """
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
     B, H, N, d = q.shape
-    Nk = k.shape[2]
+    Hkv, Nk = k.shape[1], k.shape[2]
     alpha = float(scale)
     o, lse = attn_fwd_naive(q, k, v, scale, causal, kv_lens)
     dq = np.zeros_like(q)
@@ -323,17 +344,18 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool = False, kv_lens=None):
         kvl = _kv_len(kv_lens, b, Nk)
         vis = visible(N, Nk, causal, kvl)
         for h in range(H):
-            s = alpha * (q[b, h] @ k[b, h].T)
+            hk = _kv_head(h, H, Hkv)
+            s = alpha * (q[b, h] @ k[b, hk].T)
             lse_bh = lse[b, h]
             empty = lse_bh == NEG_INF
             shift = np.where(empty, 0.0, lse_bh)
             p = np.exp(s - shift[:, None])
             p = np.where(vis & ~empty[:, None], p, 0.0)
             D = np.sum(do[b, h] * o[b, h], axis=1)
-            dv[b, h] = p.T @ do[b, h]
-            dp = do[b, h] @ v[b, h].T
+            dv[b, hk] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
             ds = p * (dp - D[:, None])
-            dq[b, h] = alpha * (ds @ k[b, h])
-            dk[b, h] = alpha * (ds.T @ q[b, h])
+            dq[b, h] = alpha * (ds @ k[b, hk])
+            dk[b, hk] += alpha * (ds.T @ q[b, h])
     return dq, dk, dv
 

@@ -62,3 +62,27 @@ def test_backward_matches_torch_autograd_fp64(causal):
     (o * torch.from_numpy(do)).sum().backward()
     for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
         assert np.max(np.abs(mine - ref.numpy())) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, "strict"])
+def test_backward_grouped_heads_unequal_lengths_finite_differences(causal):
+    """Grouped K/V heads (H = 4, H_kv = 2) and N_q = 5 < N_k = 9, bottom-right."""
+    B, H, Hkv, N, Nk, d = 1, 4, 2, 5, 9, 3
+    q, do = _rand((B, H, N, d), 91), _rand((B, H, N, d), 94)
+    k, v = _rand((B, Hkv, Nk, d), 92), _rand((B, Hkv, Nk, d), 93)
+    scale = 0.5
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, scale, causal, [8])
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, scale, causal, [8])
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, scale, causal, [8])
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.abs(fd - g) / np.maximum(1.0, np.abs(g))
+        assert np.max(err) < 1e-7, (name, np.max(err))
+    assert np.all(dk[:, :, 8:] == 0) and np.all(dv[:, :, 8:] == 0)  # padded keys

@@ -17,18 +17,25 @@ def _rand(shape, seed, scale=1.0):
 
 
 def _brute(q, k, v, scale, causal, kv_lens):
-    """Pure-Python loops with math.exp: the definition on tiny inputs."""
+    """Pure-Python loops with math.exp: the definition on tiny inputs.
+
+    K/V may have fewer heads (query head h reads K/V head h // (H / H_kv))
+    and N_k keys; query i then sits at key position i + N_k - N.
+    """
     B, H, N, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
     o = np.zeros((B, H, N, v.shape[3]))
     lse = np.zeros((B, H, N))
     for b in range(B):
-        kvl = N if kv_lens is None else int(kv_lens[b])
+        kvl = Nk if kv_lens is None else min(int(kv_lens[b]), Nk)
         for h in range(H):
+            hk = h // (H // Hkv)
             for i in range(N):
+                pos = i + Nk - N
                 if causal == "strict":
-                    keys = [j for j in range(N) if j < kvl and j < i]
+                    keys = [j for j in range(Nk) if j < kvl and j < pos]
                 else:
-                    keys = [j for j in range(N) if j < kvl and (not causal or j <= i)]
+                    keys = [j for j in range(Nk) if j < kvl and (not causal or j <= pos)]
                 if not keys:
                     o[b, h, i] = 0.0
                     lse[b, h, i] = -INF
@@ -37,13 +44,13 @@ def _brute(q, k, v, scale, causal, kv_lens):
                 for j in keys:
                     acc = 0.0
                     for t in range(d):
-                        acc += float(q[b, h, i, t]) * float(k[b, h, j, t])
+                        acc += float(q[b, h, i, t]) * float(k[b, hk, j, t])
                     sc[j] = scale * acc
                 m = max(sc.values())
                 w = {j: math.exp(sc[j] - m) for j in keys}
                 tot = sum(w.values())
                 for c in range(v.shape[3]):
-                    o[b, h, i, c] = sum(w[j] * float(v[b, h, j, c]) for j in keys) / tot
+                    o[b, h, i, c] = sum(w[j] * float(v[b, hk, j, c]) for j in keys) / tot
                 lse[b, h, i] = m + math.log(tot)
     return o, lse
 
@@ -236,3 +243,68 @@ def test_strict_causal_is_causal_shifted_by_one(kv_lens):
 def test_unknown_mask_is_rejected():
     with pytest.raises(ValueError):
         orc.visible(4, 4, "diagonal", 4)
+
+
+@pytest.mark.parametrize("causal", [False, True, "strict"])
+@pytest.mark.parametrize("H,Hkv,N,Nk", [(4, 2, 5, 9), (3, 1, 8, 8), (2, 2, 1, 7), (4, 4, 6, 3)])
+def test_grouped_heads_and_unequal_lengths_match_brute_force(causal, H, Hkv, N, Nk):
+    B, d = 2, 3
+    q = _rand((B, H, N, d), 51)
+    k, v = _rand((B, Hkv, Nk, d), 52), _rand((B, Hkv, Nk, d), 53)
+    for kv_lens in (None, [Nk, max(Nk - 2, 0)]):
+        o, lse = orc.attn_fwd_naive(q, k, v, 0.6, causal, kv_lens)
+        ob, lseb = _brute(q, k, v, 0.6, causal, kv_lens)
+        assert np.max(np.abs(o - ob)) < 1e-13
+        fin = np.isfinite(lseb)
+        assert np.array_equal(fin, np.isfinite(lse))
+        assert np.max(np.abs(lse[fin] - lseb[fin]), initial=0.0) < 1e-13
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 3])
+def test_grouped_heads_equal_repeated_kv(Hkv):
+    # H_kv < H is the same attention as H heads of K/V, each group's K/V head
+    # repeated for its query heads.
+    B, H, N, d = 2, 6, 20, 8
+    q = _rand((B, H, N, d), 61)
+    k, v, do = _rand((B, Hkv, N, d), 62), _rand((B, Hkv, N, d), 63), _rand((B, H, N, d), 64)
+    kr, vr = np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1)
+    for causal in (False, True):
+        o, lse = orc.attn_fwd_naive(q, k, v, 0.35, causal, [20, 13])
+        o2, lse2 = orc.attn_fwd_naive(q, kr, vr, 0.35, causal, [20, 13])
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.35, causal, [20, 13])
+        dq2, dk2, dv2 = orc.attn_bwd(q, kr, vr, do, 0.35, causal, [20, 13])
+        assert np.max(np.abs(dq - dq2)) < 1e-13
+        G = H // Hkv
+        assert np.max(np.abs(dk - dk2.reshape(B, Hkv, G, N, d).sum(axis=2))) < 1e-12
+        assert np.max(np.abs(dv - dv2.reshape(B, Hkv, G, N, d).sum(axis=2))) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, "strict"])
+def test_fewer_queries_are_the_last_rows_of_the_square_case(causal):
+    # Bottom-right alignment: N_q queries against N_k keys are the last N_q
+    # rows of the square causal computation whose last rows are those queries.
+    B, H, Nk, Nq, d = 2, 2, 30, 7, 6
+    k, v = _rand((B, H, Nk, d), 71), _rand((B, H, Nk, d), 72)
+    q_full = _rand((B, H, Nk, d), 73)
+    q = q_full[:, :, Nk - Nq:]
+    o, lse = orc.attn_fwd_naive(q, k, v, 0.5, causal, [30, 25])
+    of, lsef = orc.attn_fwd_naive(q_full, k, v, 0.5, causal, [30, 25])
+    assert np.array_equal(o, of[:, :, Nk - Nq:]) and np.array_equal(lse, lsef[:, :, Nk - Nq:])
+    ot, lset = orc.attn_fwd_tiled(q, k, v, 0.5, causal, [30, 25], block=4)
+    assert np.max(np.abs(ot - o)) < 1e-12
+    fin = np.isfinite(lse)
+    assert np.max(np.abs(lset[fin] - lse[fin])) < 1e-12
+
+
+def test_single_query_sees_every_key_under_the_causal_mask():
+    # Decoding: one query against N_k keys is aligned to the last position.
+    q, k, v = _rand((1, 2, 1, 8), 81), _rand((1, 2, 50, 8), 82), _rand((1, 2, 50, 8), 83)
+    o, lse = orc.attn_fwd_naive(q, k, v, 0.3, True)
+    o2, lse2 = orc.attn_fwd_naive(q, k, v, 0.3, False)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_kv_heads_must_divide_query_heads():
+    with pytest.raises(ValueError):
+        orc.attn_fwd_naive(_rand((1, 3, 4, 2), 1), _rand((1, 2, 4, 2), 2), _rand((1, 2, 4, 2), 3), 1.0)
