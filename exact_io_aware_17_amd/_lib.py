@@ -21,7 +21,7 @@ FA_ERR_HIP = -3
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_CAUSAL_STRICT = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -32,14 +32,18 @@ _f = ctypes.c_float
 # Exported symbol -> (restype, argtypes), in the order include/fa.h declares them.
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "fa_fwd_split_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
-    "fa_fwd_split": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp,
-                          ctypes.c_size_t, _vp]),
+    "fa_fwd_ex_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i]),
+    "fa_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                       ctypes.c_size_t, _vp]),
     "fa_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_fwd_f32_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                           _vp]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                     _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
 }
@@ -109,21 +113,30 @@ def default_scale(d: int) -> float:
 
 
 def _check_qkv(q, k, v):
+    """q [B, H, Nq, d]; k, v [B, Hkv, Nk, d] with H a multiple of Hkv.
+    Returns (B, H, Hkv, Nq, Nk, d)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be a GPU tensor")
         if t.dim() != 4:
-            raise ValueError(f"{name} must be [B, H, N, d]")
+            raise ValueError(f"{name} must be 4-d ([B, H, N, d])")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v must have the same shape [B, H, N, d]")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape [B, Hkv, Nk, d]")
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("q and k, v must agree in batch and head dimension")
+    if Hkv == 0 or H % Hkv != 0:
+        raise ValueError("the query heads must be a multiple of the K/V heads")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
+    return B, H, Hkv, Nq, Nk, d
 
 
 def _kv_ptr(kv_lens, B, dev):
@@ -135,21 +148,24 @@ def _kv_ptr(kv_lens, B, dev):
     return kv_lens.data_ptr()
 
 
-# Zero-filled fa_fwd_split workspaces, one per device, grown on demand: every
+# Zero-filled fa_fwd_ex workspaces, one per device, grown on demand: every
 # completed call leaves the counter region zero; calls that share one must be
 # stream-ordered, which holds for calls on one device's current stream.
 _FWD_WS = {}
 _FWD_WS_BYTES = {}
 
 
-def split_workspace_bytes(B: int, H: int, N: int, d: int, causal=False) -> int:
-    """fa_fwd_split_workspace_bytes for the current device (memoised per shape)."""
-    key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, B, H, N, d,
-           mask_kind(causal))
+def split_workspace_bytes(B: int, H: int, N: int, d: int, causal=False,
+                          Hkv: Optional[int] = None, Nk: Optional[int] = None) -> int:
+    """fa_fwd_ex_workspace_bytes for the current device (memoised per shape);
+    N is the query rows, Hkv and Nk default to H and N."""
+    Hkv = H if Hkv is None else Hkv
+    Nk = N if Nk is None else Nk
+    key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, B, H, Hkv, N, Nk,
+           d, mask_kind(causal))
     n = _FWD_WS_BYTES.get(key)
     if n is None:
-        n = int(load().fa_fwd_split_workspace_bytes(B, H, N, d,
-                                                    mask_kind(causal)))
+        n = int(load().fa_fwd_ex_workspace_bytes(B, H, Hkv, N, Nk, d, mask_kind(causal)))
         _FWD_WS_BYTES[key] = n
     return n
 
@@ -163,12 +179,13 @@ def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def schedule(N: int, BH: int, causal, cus: int, occ: int):
-    """fa_fwd_schedule: (items, nslots) of fa_fwd_split's work plan (host only)."""
+def schedule(N: int, BH: int, causal, cus: int, occ: int, Nk: Optional[int] = None):
+    """fa_fwd_schedule: (items, nslots) of fa_fwd_ex's work plan (host only);
+    N query rows, Nk keys (default N)."""
     lib = load()
     buf = (ctypes.c_uint32 * 4096)()
     ns = ctypes.c_int(0)
-    n = lib.fa_fwd_schedule(N, BH, mask_kind(causal), cus, occ, buf,
+    n = lib.fa_fwd_schedule(N, N if Nk is None else Nk, BH, mask_kind(causal), cus, occ, buf,
                             4096, ctypes.byref(ns))
     if n < 0:
         raise FaError("fa_fwd_schedule", n, status_string(n))
@@ -180,62 +197,70 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         split: bool = False, workspace: Optional[torch.Tensor] = None
         ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """fa_fwd (bfloat16) or fa_fwd_f32 (float32). Returns (O, lse).
+    """Forward of q [B, H, Nq, d] over k, v [B, Hkv, Nk, d]. Returns (O, lse).
 
-    bfloat16 with split=True calls fa_fwd_split, which may split the key range
-    of heavy query tiles over several workgroups, using `workspace` (a uint8
-    device tensor whose first 64 KiB are zero, of at least
-    split_workspace_bytes(...) bytes) or, if None, a per-device cached one.
+    bfloat16: fa_fwd when Hkv = H, Nq = Nk and split is False, else fa_fwd_ex.
+    float32: fa_fwd_f32, or fa_fwd_f32_ex for other shapes. With split=True
+    (bfloat16 only) fa_fwd_ex may split the key range of heavy query tiles
+    over several workgroups, using `workspace` (a uint8 device tensor whose
+    first 64 KiB are zero, of at least split_workspace_bytes(...) bytes) or,
+    if None, a per-device cached one.
     """
-    _check_qkv(q, k, v)
-    B, H, N, d = q.shape
+    B, H, Hkv, Nq, Nk, d = _check_qkv(q, k, v)
+    plain = (Hkv == H and Nq == Nk)
     if scale is None:
         scale = default_scale(d)
-    if q.dtype == torch.bfloat16:
-        fn_name = "fa_fwd"
-    elif q.dtype == torch.float32:
-        fn_name = "fa_fwd_f32"
-    else:
+    if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must be bfloat16 or float32")
+    if split and q.dtype != torch.bfloat16:
+        raise ValueError("split-KV is a bfloat16 path")
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
             or out.device != q.device:
         raise ValueError("out must match q")
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
             or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     kvp = _kv_ptr(kv_lens, B, q.device)
     lib = load()
     mask = mask_kind(causal)
+    tensors = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
     with torch.cuda.device(q.device):
-        if fn_name == "fa_fwd_f32":
-            st = lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                                float(scale), mask, kvp, _stream(q.device))
-        elif not split:
-            st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                            float(scale), mask, kvp, _stream(q.device))
+        stream = _stream(q.device)
+        if q.dtype == torch.float32:
+            if plain:
+                fn_name = "fa_fwd_f32"
+                st = lib.fa_fwd_f32(*tensors, B, H, Nq, d, float(scale), mask, kvp, stream)
+            else:
+                fn_name = "fa_fwd_f32_ex"
+                st = lib.fa_fwd_f32_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask, kvp,
+                                       stream)
+        elif plain and not split:
+            fn_name = "fa_fwd"
+            st = lib.fa_fwd(*tensors, B, H, Nq, d, float(scale), mask, kvp, stream)
         else:
-            fn_name = "fa_fwd_split"
+            fn_name = "fa_fwd_ex"
             ws_ptr, ws_bytes = None, 0
-            if workspace is None:
-                need = split_workspace_bytes(B, H, N, d, causal)
+            if split and workspace is None:
+                need = split_workspace_bytes(B, H, Nq, d, causal, Hkv, Nk)
                 if need > 0:
                     workspace = _fwd_workspace(q.device, need)
-            if workspace is not None:
+            if split and workspace is not None:
                 if workspace.device != q.device or not workspace.is_contiguous():
                     raise ValueError("workspace must be a contiguous tensor on q's device")
                 ws_ptr = workspace.data_ptr()
                 ws_bytes = workspace.numel() * workspace.element_size()
-            st = lib.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                                  float(scale), mask, kvp, ws_ptr, ws_bytes, _stream(q.device))
+            st = lib.fa_fwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask, kvp, ws_ptr,
+                               ws_bytes, stream)
     _check(fn_name, st)
     return out, lse
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    """fa_bwd_workspace_bytes; N is the query rows."""
     return int(load().fa_bwd_workspace_bytes(B, H, N, d))
 
 
@@ -244,31 +269,40 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """fa_bwd (bfloat16). Returns (dQ, dK, dV)."""
-    _check_qkv(q, k, v)
-    B, H, N, d = q.shape
+    """Backward (bfloat16): fa_bwd when Hkv = H and Nq = Nk, else fa_bwd_ex.
+    Returns (dQ [B, H, Nq, d], dK, dV [B, Hkv, Nk, d])."""
+    B, H, Hkv, Nq, Nk, d = _check_qkv(q, k, v)
     if q.dtype != torch.bfloat16:
-        raise ValueError("fa_bwd takes bfloat16 tensors")
+        raise ValueError("the backward takes bfloat16 tensors")
     for name, t in (("o", o), ("dout", dout)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must match q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     if scale is None:
         scale = default_scale(d)
     lib = load()
-    wsb = int(lib.fa_bwd_workspace_bytes(B, H, N, d))
+    wsb = int(lib.fa_bwd_workspace_bytes(B, H, Nq, d))
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-    elif workspace.numel() * workspace.element_size() < wsb:
-        raise ValueError(f"workspace needs {wsb} bytes")
+    elif workspace.numel() * workspace.element_size() < wsb or workspace.device != q.device \
+            or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous device tensor of {wsb} bytes")
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     kvp = _kv_ptr(kv_lens, B, q.device)
+    tensors = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+               _ptr(dv), _ptr(workspace))
     with torch.cuda.device(q.device):
-        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                        _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, float(scale),
-                        mask_kind(causal), kvp, _stream(q.device))
-    _check("fa_bwd", st)
+        stream = _stream(q.device)
+        if Hkv == H and Nq == Nk:
+            fn_name = "fa_bwd"
+            st = lib.fa_bwd(*tensors, B, H, Nq, d, float(scale), mask_kind(causal), kvp, stream)
+        else:
+            fn_name = "fa_bwd_ex"
+            st = lib.fa_bwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask_kind(causal),
+                               kvp, stream)
+    _check(fn_name, st)
     return dq, dk, dv

@@ -18,16 +18,20 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Shared checks of the shape, scale and mask arguments.
-int check_common(int B, int H, int N, int d, float scale, int mask_kind) {
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+// Shared checks of the shape, scale and mask arguments: H query heads of Nq
+// rows, Hkv K/V heads (H a multiple of Hkv) of Nk rows.
+int check_common(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
       mask_kind != FA_MASK_CAUSAL_STRICT)
     return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  // Row indices (b*H + h)*N + i are formed in 32-bit arithmetic.
-  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  // Row indices (b*H + h)*Nq + i and (b*Hkv + h)*Nk + j are formed in 32-bit
+  // arithmetic.
+  if ((long long)B * H * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -46,23 +50,25 @@ const fa::FwdPlan& no_plan() {
 }
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* workspace,
-               size_t workspace_bytes, void* stream, size_t elem, bool f32) {
+               int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream,
+               size_t elem, bool f32) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!workspace && workspace_bytes) return FA_ERR_INVALID_ARG;
-  int st = check_common(B, H, N, d, scale, mask_kind);
+  int st = check_common(B, H, Hkv, Nq, Nk, d, scale, mask_kind);
   if (st != FA_OK) return st;
-  const size_t tbytes = (size_t)B * H * N * d * elem;
-  const size_t lbytes = (size_t)B * H * N * sizeof(float);
-  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
-      overlaps(o, tbytes, v, tbytes))
+  const size_t qbytes = (size_t)B * H * Nq * d * elem;    // q, o
+  const size_t kbytes = (size_t)B * Hkv * Nk * d * elem;  // k, v
+  const size_t lbytes = (size_t)B * H * Nq * sizeof(float);
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) ||
+      overlaps(o, qbytes, v, kbytes))
     return FA_ERR_INVALID_ARG;
-  if (lse && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
-              overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
+  if (lse && (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kbytes) ||
+              overlaps(lse, lbytes, v, kbytes) || overlaps(lse, lbytes, o, qbytes)))
     return FA_ERR_INVALID_ARG;
   if (workspace) {
     const void* others[5] = {q, k, v, o, lse};
-    const size_t osz[5] = {tbytes, tbytes, tbytes, tbytes, lbytes};
+    const size_t osz[5] = {qbytes, kbytes, kbytes, qbytes, lbytes};
     for (int i = 0; i < 5; ++i)
       if (overlaps(workspace, workspace_bytes, others[i], osz[i])) return FA_ERR_INVALID_ARG;
   }
@@ -80,7 +86,9 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.kv_lens = kv_lens;
   p.B = B;
   p.H = H;
-  p.N = N;
+  p.Hkv = Hkv;
+  p.N = Nq;
+  p.Nk = Nk;
   p.d = d;
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
@@ -99,8 +107,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     const int BH = B * H;
     int cus = 0, occ = 0;
     fa::fwd_occupancy(d, p.causal != 0, &cus, &occ);
-    const fa::FwdPlan& cand = fa::fwd_plan(N, BH, p.causal != 0, cus, occ);
-    const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, N, d);
+    const fa::FwdPlan& cand = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, cus, occ);
+    const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, Nq, d);
     if (cand.nitems > 0 && workspace_bytes >= w.total) {
       plan = &cand;
       p.nslots = cand.nslots;
@@ -113,87 +121,22 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_abi_version(void) { return FA_ABI_VERSION; }
-
-const char* fa_status_string(int status) {
-  switch (status) {
-    case FA_OK:
-      return "FA_OK";
-    case FA_ERR_INVALID_ARG:
-      return "FA_ERR_INVALID_ARG: invalid argument";
-    case FA_ERR_UNSUPPORTED:
-      return "FA_ERR_UNSUPPORTED: unsupported head dimension, alignment or size";
-    case FA_ERR_HIP:
-      return "FA_ERR_HIP: kernel launch failed";
-    default:
-      return "unknown fa_status";
-  }
-}
-
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, nullptr, 0, stream, 2,
-                    false);
-}
-
-size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int mask_kind) {
-  if (check_common(B, H, N, d, 1.f, mask_kind) != FA_OK) return 0;
-  const bool causal = (mask_kind != FA_MASK_NONE);
-  int cus = 0, occ = 0;
-  fa::fwd_occupancy(d, causal, &cus, &occ);
-  const fa::FwdPlan& plan = fa::fwd_plan(N, B * H, causal, cus, occ);
-  return fa::fwd_workspace_layout(plan, B * H, N, d).total;
-}
-
-int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* workspace,
-                 size_t workspace_bytes, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, workspace,
-                    workspace_bytes, stream, 2, false);
-}
-
-int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
-               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, nullptr, 0, stream, 4,
-                    true);
-}
-
-int fa_fwd_schedule(int N, int BH, int mask_kind, int cus, int occ, uint32_t* items,
-                    int max_items, int* nslots) {
-  if (N <= 0 || BH <= 0 || cus < 0 || occ < 0 || max_items < 0 || (max_items > 0 && !items))
-    return FA_ERR_INVALID_ARG;
-  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
-      mask_kind != FA_MASK_CAUSAL_STRICT)
-    return FA_ERR_INVALID_ARG;
-  const fa::FwdPlan& plan = fa::fwd_plan(N, BH, mask_kind != FA_MASK_NONE, cus, occ);
-  for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
-  if (nslots) *nslots = plan.nslots;
-  return plan.nitems;
-}
-
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  return fa::bwd_workspace_bytes(B, H, N, d);
-}
-
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
-           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+               int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+               const int32_t* kv_lens, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
-  int st = check_common(B, H, N, d, scale, mask_kind);
+  int st = check_common(B, H, Hkv, Nq, Nk, d, scale, mask_kind);
   if (st != FA_OK) return st;
-  const size_t tbytes = (size_t)B * H * N * d * 2;
-  const size_t lbytes = (size_t)B * H * N * sizeof(float);
-  const size_t wbytes = fa::bwd_workspace_bytes(B, H, N, d);
+  const size_t qbytes = (size_t)B * H * Nq * d * 2;    // q, o, dout, dq
+  const size_t kbytes = (size_t)B * Hkv * Nk * d * 2;  // k, v, dk, dv
+  const size_t lbytes = (size_t)B * H * Nq * sizeof(float);
+  const size_t wbytes = fa::bwd_workspace_bytes(B, H, Nq, d);
   const void* ins[6] = {q, k, v, o, dout, lse};
-  const size_t insz[6] = {tbytes, tbytes, tbytes, tbytes, tbytes, lbytes};
+  const size_t insz[6] = {qbytes, kbytes, kbytes, qbytes, qbytes, lbytes};
   void* outs[4] = {dq, dk, dv, workspace};
-  const size_t outsz[4] = {tbytes, tbytes, tbytes, wbytes};
+  const size_t outsz[4] = {qbytes, kbytes, kbytes, wbytes};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_ARG;
@@ -220,7 +163,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.kv_lens = kv_lens;
   p.B = B;
   p.H = H;
-  p.N = N;
+  p.Hkv = Hkv;
+  p.N = Nq;
+  p.Nk = Nk;
   p.d = d;
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
@@ -228,6 +173,96 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
   hipError_t e = fa::launch_bwd_bf16(p, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: unsupported head dimension, alignment or size";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP: kernel launch failed";
+    default:
+      return "unknown fa_status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, scale, mask_kind, kv_lens, nullptr, 0,
+                    stream, 2, false);
+}
+
+size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int mask_kind) {
+  if (check_common(B, H, Hkv, Nq, Nk, d, 1.f, mask_kind) != FA_OK) return 0;
+  const bool causal = (mask_kind != FA_MASK_NONE);
+  int cus = 0, occ = 0;
+  fa::fwd_occupancy(d, causal, &cus, &occ);
+  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, cus, occ);
+  return fa::fwd_workspace_layout(plan, B * H, Nq, d).total;
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, mask_kind, kv_lens, workspace,
+                    workspace_bytes, stream, 2, false);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, scale, mask_kind, kv_lens, nullptr, 0,
+                    stream, 4, true);
+}
+
+int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                  int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+                  const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, mask_kind, kv_lens, nullptr, 0,
+                    stream, 4, true);
+}
+
+int fa_fwd_schedule(int Nq, int Nk, int BH, int mask_kind, int cus, int occ, uint32_t* items,
+                    int max_items, int* nslots) {
+  if (Nq <= 0 || Nk <= 0 || BH <= 0 || cus < 0 || occ < 0 || max_items < 0 ||
+      (max_items > 0 && !items))
+    return FA_ERR_INVALID_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
+      mask_kind != FA_MASK_CAUSAL_STRICT)
+    return FA_ERR_INVALID_ARG;
+  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, BH, mask_kind != FA_MASK_NONE, cus, occ);
+  for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
+  if (nslots) *nslots = plan.nslots;
+  return plan.nitems;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N, d);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H, N, N, d, scale,
+                    mask_kind, kv_lens, stream);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              const int32_t* kv_lens, void* stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk, d, scale,
+                    mask_kind, kv_lens, stream);
 }
 
 }  // extern "C"

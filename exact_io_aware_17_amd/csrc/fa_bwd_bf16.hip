@@ -184,20 +184,22 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
   if (CAUSAL) tile = ntiles - 1 - tile;  // the latest query rows see the most keys
   const int b = bh / p.H;
   const int q0 = tile * BT;
-  int kvlen = N;
-  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
+  const int Nk = p.Nk;
+  const int shift = CAUSAL ? Nk - N - p.diag : 0;  // causal: key visible iff key <= query + shift
+  int kvlen = Nk;
+  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
   int kend = kvlen;
-  if (CAUSAL) kend = min(kend, q0 + BT);
+  if (CAUSAL) kend = max(min(kend, q0 + BT + shift), 0);
   const int nblk = (kend + BS - 1) / BS;
 
   const size_t head = (size_t)bh * N * D;
+  const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
   const __bf16* Q = (const __bf16*)p.q + head;
-  const __bf16* K = (const __bf16*)p.k + head;
-  const __bf16* V = (const __bf16*)p.v + head;
+  const __bf16* K = (const __bf16*)p.k + kvhead;
+  const __bf16* V = (const __bf16*)p.v + kvhead;
   const __bf16* dO = (const __bf16*)p.dout + head;
 
   const int qa = q0 + wave * 32;
-  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
   const int qrow = qa + n;
   const int qrow_c = min(qrow, N - 1);
   bf16x8 qf[DC], of[DC];
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
 
   auto issue = [&](int j) {
     if (j >= nblk) return;
-    issue_tile<D>(K, j * BS, N, kbuf[j & 1], wave, lane);
-    issue_tile<D>(V, j * BS, N, vbuf[j & 1], wave, lane);
+    issue_tile<D>(K, j * BS, Nk, kbuf[j & 1], wave, lane);
+    issue_tile<D>(V, j * BS, Nk, vbuf[j & 1], wave, lane);
   };
   issue(0);
   for (int j = 0; j < nblk; ++j) {
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
     __syncthreads();
     issue(j + 1);
     const int key0 = j * BS;
-    if (CAUSAL && key0 + dg > qa + 31) continue;  // wholly in this wave's future
+    if (CAUSAL && key0 > qa + 31 + shift) continue;  // wholly in this wave's future
     const char* ks = kbuf[j & 1];
     const char* vs = vbuf[j & 1];
 
@@ -241,9 +243,9 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
       dp = mfma32(*(const bf16x8*)(vs + off.roff[c]), of[c], dp);
     }
     __builtin_amdgcn_s_setprio(0);
-    const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 + dg > qa);
+    const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa + shift);
     int lim = kvlen - 1;  // key visible iff key <= lim
-    if (CAUSAL) lim = min(lim, qrow - dg);
+    if (CAUSAL) lim = min(lim, qrow + shift);
     lim -= key0 + 4 * h;
     bf16x8 df[2];
 #pragma unroll
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
   if (qrow < N) store_rowT<D>((__bf16*)p.dq + head + (size_t)qrow * D, acc, p.scale, h);
 }
 
-// ---- dK, dV: one workgroup per 128 keys ----
+// ---- dK, dV: one workgroup per 128 keys of a K/V head, summed over the
+// query heads that share it ----
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int TB = BS * D * 2;
@@ -286,26 +289,24 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
-  const int N = p.N;
-  const int bh = tile_head(p.B * p.H);
-  const int tile = tile_rank(p.B * p.H);  // the earliest keys are seen by the most queries
-  const int b = bh / p.H;
+  const int N = p.N, Nk = p.Nk;
+  const int G = p.H / p.Hkv;  // query heads per K/V head
+  const int bkv = tile_head(p.B * p.Hkv);
+  const int tile = tile_rank(p.B * p.Hkv);  // the earliest keys are seen by the most queries
+  const int b = bkv / p.Hkv;
   const int kb0 = tile * BT;
-  int kvlen = N;
-  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
+  const int shift = CAUSAL ? Nk - N - p.diag : 0;  // causal: key visible iff key <= query + shift
+  int kvlen = Nk;
+  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
 
-  const size_t head = (size_t)bh * N * D;
-  const __bf16* Q = (const __bf16*)p.q + head;
-  const __bf16* K = (const __bf16*)p.k + head;
-  const __bf16* V = (const __bf16*)p.v + head;
-  const __bf16* dO = (const __bf16*)p.dout + head;
-  const float* lse2g = p.lse2 + (size_t)bh * N;
-  const float* deltag = p.delta + (size_t)bh * N;
+  const size_t kvhead = (size_t)bkv * Nk * D;
+  const size_t qhead0 = (size_t)bkv * G;  // first query head of the group (b * H + hk * G)
+  const __bf16* K = (const __bf16*)p.k + kvhead;
+  const __bf16* V = (const __bf16*)p.v + kvhead;
 
   const int kw0 = kb0 + wave * 32;
-  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
   const int key = kw0 + n;
-  const int key_c = min(key, N - 1);
+  const int key_c = min(key, Nk - 1);
   bf16x8 kf[DC], vf[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
@@ -323,30 +324,35 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
     zero(dka[t]);
   }
 
+  // Query blocks [qstart, nqb) of each of the G query heads, one stream:
+  // step u is block qstart + u % nq of group head u / nq.
   const int nqb = (N + BS - 1) / BS;
-  const int qstart = CAUSAL ? kb0 / BS : 0;
-  const int qend = (kb0 < kvlen) ? nqb : qstart;  // every key of the tile hidden: nothing to do
-  auto issue = [&](int i) {
-    if (i >= qend) return;
-    issue_tile<D>(Q, i * BS, N, qbuf[i & 1], wave, lane);
-    issue_tile<D>(dO, i * BS, N, obuf[i & 1], wave, lane);
+  const int qstart = CAUSAL ? min(max(kb0 - shift, 0) / BS, nqb) : 0;
+  const int nq = nqb - qstart;
+  const int nsteps = (kb0 < kvlen) ? G * nq : 0;  // every key of the tile hidden: nothing to do
+  auto issue = [&](int u) {
+    if (u >= nsteps) return;
+    const int g = u / nq, i = qstart + u % nq;
+    const size_t qh = qhead0 + g;
+    issue_tile<D>((const __bf16*)p.q + qh * N * D, i * BS, N, qbuf[u & 1], wave, lane);
+    issue_tile<D>((const __bf16*)p.dout + qh * N * D, i * BS, N, obuf[u & 1], wave, lane);
     if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
       const int qi = min(i * BS + (lane & 31), N - 1);
-      const float* src = (lane < 32) ? lse2g + qi : deltag + qi;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)stat[i & 1], 4, 0, 0);
+      const float* src = ((lane < 32) ? p.lse2 : p.delta) + qh * N + qi;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)stat[u & 1], 4, 0, 0);
     }
   };
-  issue(qstart);
-  for (int i = qstart; i < qend; ++i) {
+  issue(0);
+  for (int u = 0; u < nsteps; ++u) {
     wait_vmem();
     __syncthreads();
-    issue(i + 1);
-    const int qb0 = i * BS;
-    if (kw0 >= kvlen) continue;                  // all of this wave's keys are hidden
-    if (CAUSAL && kw0 + dg > qb0 + BS - 1) continue;  // every query of the block precedes them
-    const char* qs = qbuf[i & 1];
-    const char* os = obuf[i & 1];
-    const float* st = stat[i & 1];
+    issue(u + 1);
+    const int qb0 = (qstart + u % nq) * BS;
+    if (kw0 >= kvlen) continue;                         // all of this wave's keys are hidden
+    if (CAUSAL && kw0 > qb0 + BS - 1 + shift) continue;  // every query of the block precedes them
+    const char* qs = qbuf[u & 1];
+    const char* os = obuf[u & 1];
+    const float* st = stat[u & 1];
 
     // Phases in order, each value dead as soon as it is consumed: S, P, dV^T
     // (needs P), dP, dS (needs P and dP), dK^T.
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
 #pragma unroll
     for (int c = 0; c < DC; ++c) s = mfma32(*(const bf16x8*)(qs + off.roff[c]), kf[c], s);
     __builtin_amdgcn_s_setprio(0);
-    const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 + dg > qb0);
+    const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0 + shift);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int ql = 8 * g + 4 * h;  // four consecutive queries of this lane
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
         float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[e]));
         if (need_mask) {
           const int query = qb0 + ql + e;
-          if (key >= kvlen || query >= N || (CAUSAL && key + dg > query)) pr = 0.f;
+          if (key >= kvlen || query >= N || (CAUSAL && key > query + shift)) pr = 0.f;
         }
         s[r] = pr;  // P, fp32
       }
@@ -415,9 +421,9 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
   }
   wait_vmem();
 
-  if (key < N) {
-    store_rowT<D>((__bf16*)p.dk + head + (size_t)key * D, dka, p.scale, h);
-    store_rowT<D>((__bf16*)p.dv + head + (size_t)key * D, dva, 1.f, h);
+  if (key < Nk) {
+    store_rowT<D>((__bf16*)p.dk + kvhead + (size_t)key * D, dka, p.scale, h);
+    store_rowT<D>((__bf16*)p.dv + kvhead + (size_t)key * D, dva, 1.f, h);
   }
 }
 
@@ -426,15 +432,16 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
   const long long rpb = 256 / (D / 8);
   const long long g0 = (rows + rpb - 1) / rpb;
-  const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);
-  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);     // dQ: query tiles
+  const long long g2 = (long long)p.B * p.Hkv * ((p.Nk + BT - 1) / BT);  // dK, dV: key tiles
+  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
   if (p.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g2), dim3(NWB * 64), 0, stream,
                        p);
     hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g2), dim3(NWB * 64), 0, stream,
                        p);
     hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
                        p);

@@ -135,25 +135,29 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   }
   const int b = bh / p.H;
   const int q0 = tile * BM;
+  const int Nk = p.Nk;
+  // Causal: key visible iff key <= query + shift (queries are the last N of
+  // the Nk positions; the strict mask also hides the query's own position).
+  const int shift = CAUSAL ? Nk - N - p.diag : 0;
 
-  int kvlen = N;
-  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
+  int kvlen = Nk;
+  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
   int kend = kvlen;
-  if (CAUSAL) kend = min(kend, q0 + BM);
+  if (CAUSAL) kend = max(min(kend, q0 + BM + shift), 0);
   const int nblk = (kend + BN - 1) / BN;  // visible blocks
   // This item's block range: its share of the tile's nominal (unpadded)
   // blocks, clipped to the visible ones.
-  const int nbn = ((CAUSAL ? min(N, q0 + BM) : N) + BN - 1) / BN;
+  const int nbn = (max(CAUSAL ? min(Nk, q0 + BM + Nk - N) : Nk, 0) + BN - 1) / BN;
   const int jbeg = part * nbn / nparts;
   const int jend = min((part + 1) * nbn / nparts, nblk);
   const int qa = q0 + wave * 32;  // first query of this wave
   const int qrow = qa + n;
-  const int dg = CAUSAL ? p.diag : 0;  // key visible iff key <= query - dg
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D;  // Q, O rows of this head
+  const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
   const __bf16* __restrict__ Q = (const __bf16*)p.q + head;
-  const __bf16* __restrict__ K = (const __bf16*)p.k + head;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + head;
+  const __bf16* __restrict__ K = (const __bf16*)p.k + kvhead;
+  const __bf16* __restrict__ V = (const __bf16*)p.v + kvhead;
 
   // ---- Q^T fragments: lane (n, h) holds query qrow, dims 16c + 8h .. +8 ----
   bf16x8 qf[DC];
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     const int key0 = j * BN;
     char* ks = kbuf[SD];
     char* vs = vbuf[SD];
-    if (key0 + BN <= N) {
+    if (key0 + BN <= Nk) {
       const char* kb = (const char*)(K + (size_t)key0 * D);
       const char* vb = (const char*)(V + (size_t)key0 * D);
 #pragma unroll
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
         const int blk = wave * DPW + i;
         const int row = blk * ROWS_PER_DMA + lane / CPR;
         const int pch = lane % CPR;
-        const size_t key = (size_t)min(key0 + row, N - 1);
+        const size_t key = (size_t)min(key0 + row, Nk - 1);
         dma16(K + key * D + (pch ^ kswz<D>(row)) * 8, ks + blk * 1024);
         dma16(V + key * D + (pch ^ vswz<D>(row)) * 8, vs + blk * 1024);
       }
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
     const int key0 = j * BN;
     // Skip blocks wholly in this wave's future (all its rows would be masked).
-    if (CAUSAL && key0 + dg > qa + 31) return;
+    if (CAUSAL && key0 > qa + 31 + shift) return;
     const char* ks = kbuf[ST];
     const char* vs = vbuf[ST];
 
@@ -263,10 +267,10 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
     __builtin_amdgcn_s_setprio(0);
     // ---- mask (only blocks that straddle the diagonal or kv_len) ----
-    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 + dg > qa);
+    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa + shift);
     if (need_mask) {
       int lim = kvlen - 1;  // key visible iff key <= lim
-      if (CAUSAL) lim = min(lim, qrow - dg);
+      if (CAUSAL) lim = min(lim, qrow + shift);
       lim -= key0 + 4 * h;
 #pragma unroll
       for (int t = 0; t < KT; ++t)

@@ -37,16 +37,22 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
   const int qrow = q0 + (tid >> 1);
   const int qrow_c = min(qrow, N - 1);
 
-  int kvlen = N;
-  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), N);
+  const int Nk = p.Nk;
+  // Causal: key visible iff key <= query + shift (the queries are the last N
+  // of the Nk positions; the strict mask also hides the query's own one).
+  const int shift = CAUSAL ? Nk - N - p.diag : 0;
+
+  int kvlen = Nk;
+  if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
   int kend = kvlen;
-  if (CAUSAL) kend = min(kend, q0 + BQ);
+  if (CAUSAL) kend = max(min(kend, q0 + BQ + shift), 0);
   const int nblk = (kend + BK - 1) / BK;
 
   const size_t head = (size_t)bh * N * D;
+  const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
   const float* Q = (const float*)p.q + head;
-  const float* K = (const float*)p.k + head;
-  const float* V = (const float*)p.v + head;
+  const float* K = (const float*)p.k + kvhead;
+  const float* V = (const float*)p.v + kvhead;
 
   float q[HD];
 #pragma unroll
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
     __syncthreads();
     for (int u = tid; u < BK * D; u += 256) {
       const int r = u / D, c = u % D;
-      const int key = min(key0 + r, N - 1);
+      const int key = min(key0 + r, Nk - 1);
       ks[r][c] = K[(size_t)key * D + c];
       vs[r][c] = V[(size_t)key * D + c];
     }
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdParams p) {
       for (int t = 0; t < HD; ++t) dot = fmaf(q[t], ks[jj][half * HD + t], dot);
       dot += __shfl_xor(dot, 1);
       const int key = key0 + jj;
-      const bool vis = (key < kvlen) && (!CAUSAL || key + p.diag <= qrow);
+      const bool vis = (key < kvlen) && (!CAUSAL || key <= qrow + shift);
       const float s = vis ? dot * scale : NEG_INF;
       sc[jj] = s;
       bmax = fmaxf(bmax, s);

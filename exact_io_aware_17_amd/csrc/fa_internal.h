@@ -14,10 +14,11 @@ struct FwdParams {
   void* o;
   float* lse;              // may be null
   const int32_t* kv_lens;  // may be null
-  int B, H, N, d;
+  int B, H, N, d;          // N: query rows per head
+  int Hkv, Nk;             // K/V heads (a divisor of H) and key rows per head
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
-  int causal;              // key j visible to query i only if j <= i - diag
+  int causal;              // key j visible to query i only if j <= i + Nk - N - diag
   int diag;                // 0: causal (j <= i), 1: strict causal (j < i)
   // Split work items (used only with a plan of nitems > 0): per (b, h)
   // nslots partial states, each BM rows of unnormalised O (fp32) plus the
@@ -49,11 +50,12 @@ struct FwdPlan {
   uint32_t item[FWD_PLAN_MAX];
 };
 
-// Balancing plan for N query rows, BH heads, `cus` compute units and `occ`
-// resident workgroups per compute unit (cached; the reference stays valid).
-const FwdPlan& fwd_plan(int N, int BH, bool causal, int cus, int occ);
-// Nominal key blocks of query tile t.
-int fwd_tile_blocks(int N, int t, bool causal);
+// Balancing plan for N query rows against Nk keys, BH query heads, `cus`
+// compute units and `occ` resident workgroups per compute unit (cached; the
+// reference stays valid).
+const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int cus, int occ);
+// Nominal key blocks of query tile t (causal: bottom-right aligned).
+int fwd_tile_blocks(int N, int Nk, int t, bool causal);
 // Workspace layout for a plan: byte offsets of counters, part_ml, part_o and the total.
 struct FwdWorkspace {
   size_t counters, part_ml, part_o, total;
@@ -76,7 +78,8 @@ struct BwdParams {
   float* delta;            // workspace: D_i = sum_c dO_ic O_ic, [B, H, N] float32
   float* lse2;             // workspace: lse_i * log2(e) (+inf for an empty row), [B, H, N]
   const int32_t* kv_lens;
-  int B, H, N, d;
+  int B, H, N, d;          // N: query rows per head
+  int Hkv, Nk;             // as FwdParams
   float scale;
   float scale_log2;
   int causal;

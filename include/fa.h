@@ -15,32 +15,43 @@
  * A row with no visible key returns O_i = 0 and lse_i = -inf ("Worked
  * examples", Cell D2, the guard).
  *
- * Visibility: key j is visible to query i iff
- *   (mask_kind != FA_MASK_CAUSAL || j <= i)  &&
- *   (mask_kind != FA_MASK_CAUSAL_STRICT || j < i)  &&  j < kv_len_b,
- * where kv_len_b = kv_lens[b] clamped to [0, N] (kv_lens == NULL means N).
- * Causal masking is top-left aligned (queries and keys share positions
- * 0..N-1). Padding hides keys only; every query row is computed.
+ * Shapes: B batches, H query heads of Nq rows each, Hkv key/value heads of
+ * Nk rows each, head dimension d. H must be a multiple of Hkv; query head h
+ * attends to K/V head h / (H / Hkv) (Hkv = H: multi-head; 1 < Hkv < H:
+ * grouped K/V heads; Hkv = 1: one K/V head shared by all). Attention runs per
+ * query head exactly as for one head ("Question bank": the method is applied
+ * per head unchanged inside multi-head attention). The plain entry points
+ * (fa_fwd, fa_fwd_f32, fa_bwd) are the case Hkv = H, Nq = Nk = N.
  *
- * Layout: every tensor is contiguous [B, H, N, d] (d innermost), lse is
- * contiguous [B, H, N] float32. Pointers are device pointers allocated by
- * the caller (the library allocates and frees no device memory; on the host
- * it caches per-shape work plans and per-device occupancy, guarded by a
- * mutex). Tensor and workspace base pointers must be 16-byte aligned.
+ * Visibility: key j is visible to query i iff j < kv_len_b and
+ *   FA_MASK_CAUSAL:         j <= i + (Nk - Nq)
+ *   FA_MASK_CAUSAL_STRICT:  j <  i + (Nk - Nq)
+ * where kv_len_b = kv_lens[b] clamped to [0, Nk] (kv_lens == NULL means Nk).
+ * With Nq = Nk this is the usual j <= i (j < i); with Nq < Nk the queries are
+ * the last Nq of the Nk positions (a continuation after a cached prefix:
+ * Nq = 1 sees every key). With Nq > Nk the first Nq - Nk queries see no key.
+ * Padding hides keys only; every query row is computed.
+ *
+ * Layout: q, o (and dout, dq) are contiguous [B, H, Nq, d]; k, v (and dk, dv)
+ * contiguous [B, Hkv, Nk, d] (d innermost); lse is contiguous [B, H, Nq]
+ * float32. Pointers are device pointers allocated by the caller (the library
+ * allocates and frees no device memory; on the host it caches per-shape work
+ * plans and per-device occupancy, guarded by a mutex). Tensor and workspace
+ * base pointers must be 16-byte aligned.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
  * Faults inside a kernel surface at the caller's next synchronisation.
  *
  * Errors are returned before anything is enqueued:
- *   FA_ERR_INVALID_ARG  null tensor pointer, B/H/N <= 0, scale not finite
- *                       or not > 0, unknown mask_kind, an output overlapping
- *                       an input;
+ *   FA_ERR_INVALID_ARG  null tensor pointer, B/H/Hkv/Nq/Nk <= 0, H not a
+ *                       multiple of Hkv, scale not finite or not > 0,
+ *                       unknown mask_kind, an output overlapping an input;
  *   FA_ERR_UNSUPPORTED  d not supported (64 and 128 are), a tensor pointer
  *                       not 16-byte aligned, sizes whose element count does
  *                       not fit the kernels' 32-bit row indices;
  *   FA_ERR_HIP          the launch itself failed (hipGetLastError).
- * kv_lens values outside [0, N] are clamped by the kernels.
+ * kv_lens values outside [0, Nk] are clamped by the kernels.
  */
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
@@ -52,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_OK = 0,
@@ -63,10 +74,12 @@ typedef enum {
 
 typedef enum {
   FA_MASK_NONE = 0,          /* every key visible (subject to kv_lens) */
-  FA_MASK_CAUSAL = 1,        /* key j visible to query i iff j <= i */
-  FA_MASK_CAUSAL_STRICT = 2  /* key j visible to query i iff j < i: the variant
-                                of "Worked examples", Cell D2, whose first row
-                                sees no key (O = 0, lse = -inf) */
+  FA_MASK_CAUSAL = 1,        /* key j visible to query i iff j <= i
+                                (+ Nk - Nq) */
+  FA_MASK_CAUSAL_STRICT = 2  /* key j visible to query i iff j < i (+ Nk - Nq):
+                                the variant of "Worked examples", Cell D2,
+                                whose first row sees no key (O = 0,
+                                lse = -inf) */
 } fa_mask_kind;
 
 /*
@@ -87,37 +100,41 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const int32_t* kv_lens, void* stream);
 
 /*
- * Bytes of workspace fa_fwd_split needs for these sizes on the current
- * device; 0 when its plan does not split any tile (then fa_fwd_split is
- * fa_fwd), or for invalid arguments.
+ * Bytes of workspace fa_fwd_ex needs for these sizes on the current device
+ * to split key ranges; 0 when its plan does not split any tile (then no
+ * workspace is needed), or for invalid arguments.
  */
-size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int mask_kind);
+size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int mask_kind);
 
 /*
- * fa_fwd with the key range of the heaviest query tiles split over several
- * workgroups (split-KV): each part streams its share of the keys, stores its
- * partial softmax state (row max, both row sums, unnormalised output; fp32)
- * in the workspace, and the last part of a tile to finish merges all parts
- * with the exact block merge ("Exercises" of the interactive explainer "The
- * Flash Attention", the block merges) in part order. For grids too small to
- * fill the GPU (few heads, long rows) this spreads a tile over several
- * compute units. Same tensors and results as fa_fwd up to rounding; bitwise
- * reproducible for a given device and shape.
- *   workspace       : device memory, or NULL with workspace_bytes = 0. With
- *                     fewer than fa_fwd_split_workspace_bytes(...) bytes no
- *                     tile is split. Its first 64 KiB hold arrival counters
- *                     that must be zero before the first use; every completed
- *                     call leaves them zero, for any later shape (the rest is
- *                     scratch). Calls sharing a workspace must be ordered
- *                     (same stream, or synchronised). It must not overlap any
- *                     tensor argument.
+ * fa_fwd for grouped K/V heads (Hkv) and Nq != Nk (see the shapes and
+ * visibility above), with optional split-KV: given a workspace, the key range
+ * of the heaviest query tiles is split over several workgroups; each part
+ * streams its share of the keys, stores its partial softmax state (row max,
+ * both row sums, unnormalised output; fp32) in the workspace, and the last
+ * part of a tile to finish merges all parts with the exact block merge
+ * ("Exercises" of the interactive explainer "The Flash Attention", the block
+ * merges) in part order. For grids too small to fill the GPU (few heads,
+ * long rows, short decode queries over long caches) this spreads a tile over
+ * several compute units. Same results as without the split up to rounding;
+ * bitwise reproducible for a given device and shape.
+ *   q, o      : [B, H, Nq, d] bfloat16;  k, v : [B, Hkv, Nk, d] bfloat16
+ *   lse       : [B, H, Nq] float32 or NULL
+ *   kv_lens   : device int32 [B] valid key counts (clamped to [0, Nk]), or NULL
+ *   workspace : device memory, or NULL with workspace_bytes = 0 (no split).
+ *               With fewer than fa_fwd_ex_workspace_bytes(...) bytes no tile
+ *               is split. Its first 64 KiB hold arrival counters that must be
+ *               zero before the first use; every completed call leaves them
+ *               zero, for any later shape (the rest is scratch). Calls
+ *               sharing a workspace must be ordered (same stream, or
+ *               synchronised). It must not overlap any tensor argument.
  * Errors as fa_fwd, and FA_ERR_INVALID_ARG for workspace_bytes > 0 with a
  * NULL workspace, FA_ERR_UNSUPPORTED for a workspace not 16-byte aligned.
  */
-int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
-                 int B, int H, int N, int d, float scale, int mask_kind,
-                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
-                 void* stream);
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+              void* stream);
 
 /*
  * The same contract with float32 q, k, v, o (float32 arithmetic throughout).
@@ -126,9 +143,15 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
 
+/* fa_fwd_f32 for grouped K/V heads and Nq != Nk (shapes as fa_fwd_ex). */
+int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse,
+                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+                  const int32_t* kv_lens, void* stream);
+
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (caller-allocated,
- * at least 256-byte aligned; contents need not be initialised).
+ * at least 256-byte aligned; contents need not be initialised). For
+ * fa_bwd_ex pass the query rows: fa_bwd_workspace_bytes(B, H, Nq, d).
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -150,8 +173,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const int32_t* kv_lens, void* stream);
 
 /*
- * Host-only view of fa_fwd_split's work plan (no device call): for N query
- * rows, BH = B*H heads, mask_kind, `cus` compute units and `occ` resident
+ * fa_bwd for grouped K/V heads and Nq != Nk (shapes as fa_fwd_ex):
+ *   q, o, dout, dq : [B, H, Nq, d] bfloat16;  k, v, dk, dv : [B, Hkv, Nk, d]
+ *   lse            : [B, H, Nq] float32 from fa_fwd / fa_fwd_ex
+ *   workspace      : fa_bwd_workspace_bytes(B, H, Nq, d) bytes
+ * dK and dV of a K/V head are the sums over the H / Hkv query heads that
+ * share it (each such head uses the same K, V rows, so their gradient
+ * contributions add).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, void* workspace,
+              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              const int32_t* kv_lens, void* stream);
+
+/*
+ * Host-only view of fa_fwd_ex's work plan (no device call): for Nq query
+ * rows and Nk keys, BH = B*H query heads, mask_kind, `cus` compute units and
+ * `occ` resident
  * workgroups per compute unit, returns the number of work items (0 = one
  * item per query tile, no split) and copies up to max_items of them to
  * `items`, each
@@ -159,7 +197,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * in dispatch order; *nslots receives the partial-state slots per head.
  * Returns FA_ERR_INVALID_ARG for invalid arguments.
  */
-int fa_fwd_schedule(int N, int BH, int mask_kind, int cus, int occ, uint32_t* items,
+int fa_fwd_schedule(int Nq, int Nk, int BH, int mask_kind, int cus, int occ, uint32_t* items,
                     int max_items, int* nslots);
 
 /* Human-readable name of a status code (static storage). */

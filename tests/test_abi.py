@@ -49,14 +49,20 @@ def test_workspace_bytes():
 
 
 def _fwd(fn="fa_fwd", q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ,
-         B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None, ws=None, ws_bytes=0):
+         B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None, ws=None, ws_bytes=0, Hkv=None,
+         Nk=None):
     lib = _lib.load()
-    if fn == "fa_fwd_split":
-        return lib.fa_fwd_split(q, k, v, o, lse, B, H, N, d, scale, mask, kv, ws, ws_bytes, None)
+    Hkv = H if Hkv is None else Hkv
+    Nk = N if Nk is None else Nk
+    if fn == "fa_fwd_ex":
+        return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, scale, mask, kv, ws, ws_bytes,
+                             None)
+    if fn == "fa_fwd_f32_ex":
+        return lib.fa_fwd_f32_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, scale, mask, kv, None)
     return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, scale, mask, kv, None)
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_split", "fa_fwd_f32"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_fwd_f32_ex"])
 def test_fwd_argument_errors(fn):
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
     assert _fwd(fn, q=None) == INV
@@ -79,9 +85,26 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, B=1 << 16, H=1 << 16, N=1) == UNS  # row count beyond 32-bit
 
 
+@pytest.mark.parametrize("fn", ["fa_fwd_ex", "fa_fwd_f32_ex"])
+def test_grouped_shape_argument_errors(fn):
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    assert _fwd(fn, H=8, Hkv=0) == INV
+    assert _fwd(fn, H=8, Hkv=3) == INV              # H not a multiple of Hkv
+    assert _fwd(fn, H=2, Hkv=4) == INV
+    assert _fwd(fn, Nk=0) == INV
+    assert _fwd(fn, Nk=-5) == INV
+    assert _fwd(fn, B=1 << 12, H=1, Nk=1 << 20) == UNS  # key rows beyond 32-bit
+    # o at k + 1 KiB: inside k only when k's extent is taken from Nk (16 rows
+    # of d=64 are 2 KiB in bf16), not from Nq = 4.
+    assert _fwd(fn, N=4, Nk=16, o=A + SZ + 1024) == INV
+    assert _fwd(fn, N=4, Nk=16, lse=A + 2 * SZ + 1024) == INV  # lse inside v
+    # k is [1, 2, 16, 64] bf16 = 4 KiB: o over its last 16 bytes.
+    assert _fwd(fn, H=8, Hkv=2, o=A + SZ + 2 * 16 * 64 * 2 - 16) == INV
+
+
 def test_split_workspace_argument_errors():
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
-    f = "fa_fwd_split"
+    f = "fa_fwd_ex"
     assert _fwd(f, ws=None, ws_bytes=256) == INV            # size without a pointer
     assert _fwd(f, ws=A + 16, ws_bytes=SZ) == INV           # workspace overlaps q
     assert _fwd(f, ws=A + 3 * SZ + 64, ws_bytes=256) == INV  # workspace overlaps o
@@ -91,9 +114,11 @@ def test_split_workspace_argument_errors():
 
 def test_split_workspace_bytes_invalid_sizes():
     lib = _lib.load()
-    assert lib.fa_fwd_split_workspace_bytes(0, 16, 4096, 128, 1) == 0
-    assert lib.fa_fwd_split_workspace_bytes(2, 16, 4096, 96, 1) == 0
-    assert lib.fa_fwd_split_workspace_bytes(2, 16, 4096, 128, 7) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(0, 16, 16, 4096, 4096, 128, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 96, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 128, 7) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 3, 4096, 4096, 128, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 0, 128, 1) == 0
 
 
 def test_bwd_argument_errors():
@@ -122,6 +147,32 @@ def test_bwd_argument_errors():
     p = list(base)
     p[9] = base[9] + 8        # workspace misaligned
     assert call(p) == UNS
+
+
+def test_bwd_ex_argument_errors():
+    lib = _lib.load()
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    base = [A + i * SZ for i in range(10)]
+
+    def call(ptrs=None, B=1, H=4, Hkv=2, Nq=16, Nk=32, d=64, scale=0.125, mask=1):
+        p = list(base if ptrs is None else ptrs)
+        return lib.fa_bwd_ex(*p, B, H, Hkv, Nq, Nk, d, scale, mask, None, None)
+
+    assert call(Hkv=3) == INV
+    assert call(Hkv=0) == INV
+    assert call(Nk=0) == INV
+    assert call(Nq=0) == INV
+    assert call(d=32) == UNS
+    # k is [1, 2, 32, 64] bf16 = 8 KiB: dk over its last 16 bytes, and dk just
+    # past its end, which overlaps it once k has 33 rows.
+    p = list(base)
+    p[7] = base[1] + 8192 - 16
+    assert call(p) == INV
+    p[7] = base[1] + 8192
+    assert call(p, Nk=33) == INV
+    p = list(base)
+    p[8] = base[6] + 4 * 16 * 64 * 2 - 16    # dv inside dq ([1, 4, 16, 64] bf16)
+    assert call(p) == INV
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

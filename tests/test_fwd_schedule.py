@@ -1,8 +1,9 @@
-"""fa_fwd_split's host-side work plan (fa_fwd_schedule; no device involved).
+"""fa_fwd_ex's host-side work plan (fa_fwd_schedule; no device involved).
 
 Every query tile must be covered exactly once: its nominal key blocks
-(ceil(min(N, 128 (t+1)) / 32) under the causal mask, ceil(N / 32) without)
-are partitioned by the parts of the tile, split tiles own disjoint
+(ceil(min(Nk, 128 (t+1) + Nk - Nq) / 32) under the causal mask, the queries
+being the last Nq of Nk positions; ceil(Nk / 32) without) are partitioned by
+the parts of the tile, split tiles own disjoint
 partial-state slots, and the items come longest first under the planner's
 stated cost model. The schedule simulation that chose the plan is
 re-implemented here from its description (compute units of `occ` slots whose
@@ -22,8 +23,9 @@ ITEM, SPLIT = 2.0, 7.0   # cost per item and extra per split part, in key blocks
 MIN_GAIN = 0.75
 
 
-def tile_blocks(N, t, causal):
-    kend = min(N, BM * (t + 1)) if causal else N
+def tile_blocks(N, t, causal, Nk=None):
+    Nk = N if Nk is None else Nk
+    kend = max(0, min(Nk, BM * (t + 1) + Nk - N)) if causal else Nk
     return math.ceil(kend / BN)
 
 
@@ -75,33 +77,38 @@ def simulate(costs, BH, cus, occ):
     return end
 
 
+# (Nq, Nk, BH, causal, cus, occ)
 CASES = [
-    (4096, 32, True, 256, 3),     # the metric shape: several waves of work, not split
-    (4096, 32, False, 256, 3),
-    (16384, 2, True, 256, 3),     # few heads, long rows: split
-    (16384, 1, False, 256, 3),
-    (8192, 4, True, 256, 3),
-    (1000, 6, True, 256, 3),      # ragged last tile
-    (1024, 1, False, 256, 3),
-    (640, 4, False, 256, 5),
-    (64, 1, True, 256, 3),
-    (4096, 32, True, 0, 0),       # unknown device: never split
-    (65536, 64, True, 256, 3),    # many waves of work: never split
+    (4096, 4096, 32, True, 256, 3),     # the metric shape: several waves of work, not split
+    (4096, 4096, 32, False, 256, 3),
+    (16384, 16384, 2, True, 256, 3),    # few heads, long rows: split
+    (16384, 16384, 1, False, 256, 3),
+    (8192, 8192, 4, True, 256, 3),
+    (1000, 1000, 6, True, 256, 3),      # ragged last tile
+    (1024, 1024, 1, False, 256, 3),
+    (640, 640, 4, False, 256, 5),
+    (64, 64, 1, True, 256, 3),
+    (4096, 4096, 32, True, 0, 0),       # unknown device: never split
+    (65536, 65536, 64, True, 256, 3),   # many waves of work: never split
+    (1, 32768, 32, True, 256, 3),       # one decode query per head over a long cache
+    (16, 8192, 8, False, 256, 3),
+    (1024, 8192, 4, True, 256, 3),      # a continuation after a 7168-key prefix
+    (2048, 1000, 2, True, 256, 3),      # Nq > Nk: early query tiles see no key
 ]
 
 
-def _costs(items, N, causal):
+def _costs(items, N, Nk, causal):
     out = []
     for it in items:
         t, part, np_, _ = decode(it)
-        nb = tile_blocks(N, t, causal)
+        nb = tile_blocks(N, t, causal, Nk)
         out.append((part + 1) * nb // np_ - part * nb // np_ + ITEM + (SPLIT if np_ > 1 else 0))
     return out
 
 
-@pytest.mark.parametrize("N,BH,causal,cus,occ", CASES)
-def test_plan_covers_every_tile_once(N, BH, causal, cus, occ):
-    items, nslots = _lib.schedule(N, BH, causal, cus, occ)
+@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ", CASES)
+def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ):
+    items, nslots = _lib.schedule(N, BH, causal, cus, occ, Nk)
     ntiles = math.ceil(N / BM)
     if not items:
         return
@@ -118,12 +125,12 @@ def test_plan_covers_every_tile_once(N, BH, causal, cus, occ):
         np_ = ps[0][1]
         assert sorted(p for p, _, _ in ps) == list(range(np_))
         assert all(n == np_ for _, n, _ in ps)
-        nb = tile_blocks(N, t, causal)
+        nb = tile_blocks(N, t, causal, Nk)
         ranges = sorted((p * nb // np_, (p + 1) * nb // np_) for p, _, _ in ps)
         assert ranges[0][0] == 0 and ranges[-1][1] == nb
         assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
-        assert all(lo < hi for lo, hi in ranges)  # no empty nominal part
         if np_ > 1:
+            assert all(lo < hi for lo, hi in ranges)  # no empty nominal part
             sb = ps[0][2]
             assert all(s == sb for _, _, s in ps)
             slots_t = set(range(sb, sb + np_))
@@ -132,15 +139,15 @@ def test_plan_covers_every_tile_once(N, BH, causal, cus, occ):
             assert sb + np_ <= nslots
 
 
-@pytest.mark.parametrize("N,BH,causal,cus,occ", CASES)
-def test_plan_is_longest_first_and_pays_off(N, BH, causal, cus, occ):
-    items, _ = _lib.schedule(N, BH, causal, cus, occ)
+@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ", CASES)
+def test_plan_is_longest_first_and_pays_off(N, Nk, BH, causal, cus, occ):
+    items, _ = _lib.schedule(N, BH, causal, cus, occ, Nk)
     if not items:
         return
-    costs = _costs(items, N, causal)
+    costs = _costs(items, N, Nk, causal)
     assert all(a >= b for a, b in zip(costs, costs[1:]))
     ntiles = math.ceil(N / BM)
-    unsplit = sorted((tile_blocks(N, t, causal) + ITEM for t in range(ntiles)), reverse=True)
+    unsplit = sorted((tile_blocks(N, t, causal, Nk) + ITEM for t in range(ntiles)), reverse=True)
     assert simulate(costs, BH, cus, occ) < MIN_GAIN * simulate(unsplit, BH, cus, occ)
 
 
@@ -150,14 +157,19 @@ def test_split_only_underfilled_grids():
     assert len(items) > 128 and nslots > 0
     assert _lib.schedule(16384, 2, True, 256, 3) == (items, nslots)  # cached, deterministic
     assert max(decode(it)[2] for it in _lib.schedule(1024, 1, False, 256, 3)[0]) == 4
+    # Decode (one query per head) over a long cache: every head's only tile split.
+    items, nslots = _lib.schedule(1, 32, True, 256, 3, 32768)
+    assert len(items) == 4 and nslots == 4
+    assert _lib.schedule(1, 32, True, 256, 3, 32768) != _lib.schedule(1, 32, True, 256, 3, 1)
 
 
 def test_schedule_argument_errors():
     lib = _lib.load()
     INV = _lib.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(0, 1, 1, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 0, 1, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 1, 5, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 1, 1, -1, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 1, 1, 256, -3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 1, 1, 256, 3, None, 4, None) == INV
+    assert lib.fa_fwd_schedule(0, 128, 1, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 0, 1, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 0, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 5, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 1, -1, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 1, 256, -3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 1, 256, 3, None, 4, None) == INV
