@@ -7,7 +7,7 @@ Q/K/V iid N(0,1) from a seeded CPU generator, already resident in device
 memory when timing starts. A timed step is one fa_fwd launch over the whole
 batch (value = forward TFLOP/s at 4*B*H*N^2*d/2 FLOPs). The backward pass is
 timed the same way and reported beside it ("bwd"), together with one full
-forward+backward pass ("fwd_bwd_step"), fa_fwd_split is compared with
+forward+backward pass ("fwd_bwd_step"), fa_fwd_ex (split-KV) is compared with
 fa_fwd on a grid too small to fill the GPU ("split_kv"), and a naive forward
 that materialises S and P in device memory (PyTorch matmul + softmax, the
 comparison path, not part of libfa) is timed on the same inputs ("naive").
@@ -235,7 +235,7 @@ def naive_comparison(w, q, k, v, o, stream, reps=5):
 
 
 def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
-    """fa_fwd vs fa_fwd_split on a causal grid too small to fill the GPU."""
+    """fa_fwd vs fa_fwd_ex with the split-KV workspace on a causal grid too small to fill the GPU."""
     import torch
     import exact_io_aware_17_amd as fa
     from exact_io_aware_17_amd import workloads as W
@@ -247,7 +247,7 @@ def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
     flops = W.fwd_flops(B, H, N, d, True)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    for name, split in (("fa_fwd", False), ("fa_fwd_split", True)):
+    for name, split in (("fa_fwd", False), ("fa_fwd_ex_split", True)):
         for _ in range(3):
             fa.fwd(q, k, v, causal=True, split=split)
         torch.cuda.synchronize()
@@ -270,7 +270,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
-                    help="skip the fa_fwd_split comparison (it launches the forward kernel "
+                    help="skip the split-KV comparison (it launches the forward kernel "
                          "at another shape)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run (copy calibration + forward) for rocprofv3 counters")

@@ -1,7 +1,7 @@
-"""GPU parity of fa_fwd_split (split-KV): the heaviest query tiles cut into key
+"""GPU parity of split-KV (fa_fwd_ex with a workspace): the heaviest query tiles cut into key
 ranges whose partial states are merged by the last part to arrive.
 
-Both entry points (fa_fwd_split, and fa_fwd with one workgroup per tile) are
+Both paths (fa_fwd_ex with the workspace, and fa_fwd with one workgroup per tile) are
 compared with the fp64 oracle on the same inputs; the split path must be
 bitwise reproducible and must leave its arrival counters at zero. The shapes
 have few heads, so that the plan splits them.
@@ -105,5 +105,5 @@ def test_short_workspace_runs_unsplit():
 
 
 def test_metric_shape_is_not_split():
-    # Several waves of workgroups: fa_fwd_split runs one workgroup per tile.
+    # Several waves of workgroups: the plan keeps one workgroup per tile.
     assert fa.split_workspace_bytes(2, 16, 4096, 128, True) == 0
