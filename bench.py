@@ -36,8 +36,9 @@ SWEEP_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_bh32d128_traffic_sw
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)  # causal, B=2, H=16, d=128
 KERNEL_SOURCES = [
     os.path.join(ROOT, "exact_io_aware_17_amd", "csrc", f)
-    for f in ("fa_fwd_bf16.hip", "fa_device.h", "fa_internal.h")
+    for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")
 ]
+FWD_KERNEL_TAG = "fwd_kernel<"  # the forward kernel's name in profiler output
 
 
 def kernel_source_hash() -> str:
@@ -162,16 +163,16 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
     per_key = {}
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         rows = read(d, counter)
-        first_fwd = min((i for i, n, _ in rows if "fwd_bf16" in n), default=-1)
+        first_fwd = min((i for i, n, _ in rows if FWD_KERNEL_TAG in n), default=-1)
         copy = [v for i, n, v in rows
-                if i < first_fwd and "fwd_bf16" not in n and v > 0.5 * COPY_BYTES / 1024]
-        fwd = [v for _, n, v in rows if "fwd_bf16" in n]
+                if i < first_fwd and FWD_KERNEL_TAG not in n and v > 0.5 * COPY_BYTES / 1024]
+        fwd = [v for _, n, v in rows if FWD_KERNEL_TAG in n]
         if not copy or len(fwd) != 3 + len(SWEEP_N):
             print(f"{counter}: expected copy readings and {3 + len(SWEEP_N)} forward "
                   f"dispatches, got {len(copy)} and {len(fwd)}", file=sys.stderr)
             return 1
         scale = COPY_BYTES / (sorted(copy)[len(copy) // 2] * 1024.0)
-        last_fwd = max(i for i, n, _ in rows if "fwd_bf16" in n)
+        last_fwd = max(i for i, n, _ in rows if FWD_KERNEL_TAG in n)
         naive = sum(v for i, _, v in rows if i > last_fwd) * 1024.0 * scale
         out["naive_" + key + "_bytes"] = naive
         wl = sorted(fwd[:3])[1]
@@ -360,7 +361,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_bf16_kernel<128, 32, 2, true>",
+            "kernel": "fwd_kernel<__bf16, 128, 32, 2, true>",
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_kernel, 5),
             "kernel_ms_min": round(per_launch[0], 5),

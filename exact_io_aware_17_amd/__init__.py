@@ -1,12 +1,16 @@
 """MI355X-native exact attention: libfa (C-ABI, gfx950 HIP kernels) and its binding.
 
     from exact_io_aware_17_amd import fwd, bwd
-    o, lse = fwd(q, k, v, causal=True)              # bf16 or fp32 [B, H, N, d] GPU tensors
+    o, lse = fwd(q, k, v, causal=True)    # bf16, fp16 or fp32 GPU tensors: q [B, H, Nq, d],
+                                          # k, v [B, Hkv, Nk, d]
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
 
 The library is loaded on first use; importing this package touches no GPU.
 """
 from ._lib import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_F16,
+    FA_DTYPE_F32,
     FA_ERR_HIP,
     FA_ERR_INVALID_ARG,
     FA_ERR_UNSUPPORTED,
@@ -18,6 +22,7 @@ from ._lib import (  # noqa: F401
     bwd,
     bwd_workspace_bytes,
     default_scale,
+    dtype_code,
     fwd,
     load,
     mask_kind,

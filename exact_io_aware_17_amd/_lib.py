@@ -21,7 +21,10 @@ FA_ERR_HIP = -3
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_CAUSAL_STRICT = 2
-ABI_VERSION = 3
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F16 = 1
+FA_DTYPE_F32 = 2
+ABI_VERSION = 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -32,17 +35,15 @@ _f = ctypes.c_float
 # Exported symbol -> (restype, argtypes), in the order include/fa.h declares them.
 SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "fa_fwd_ex_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i]),
-    "fa_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+    "fa_fwd_ex_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "fa_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                        ctypes.c_size_t, _vp]),
     "fa_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "fa_fwd_f32_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
-                           _vp]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                     _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                       _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+                       _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
@@ -107,6 +108,17 @@ def mask_kind(causal) -> int:
     return FA_MASK_CAUSAL if causal else FA_MASK_NONE
 
 
+_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16,
+           torch.float32: FA_DTYPE_F32}
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    """fa_dtype of a torch dtype (bfloat16, float16 or float32)."""
+    if dtype not in _DTYPES:
+        raise ValueError("tensors must be bfloat16, float16 or float32")
+    return _DTYPES[dtype]
+
+
 def default_scale(d: int) -> float:
     """float32(1/sqrt(d)), the value every path receives."""
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
@@ -156,16 +168,18 @@ _FWD_WS_BYTES = {}
 
 
 def split_workspace_bytes(B: int, H: int, N: int, d: int, causal=False,
-                          Hkv: Optional[int] = None, Nk: Optional[int] = None) -> int:
+                          Hkv: Optional[int] = None, Nk: Optional[int] = None,
+                          dtype: torch.dtype = torch.bfloat16) -> int:
     """fa_fwd_ex_workspace_bytes for the current device (memoised per shape);
     N is the query rows, Hkv and Nk default to H and N."""
     Hkv = H if Hkv is None else Hkv
     Nk = N if Nk is None else Nk
+    code = dtype_code(dtype)
     key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, B, H, Hkv, N, Nk,
-           d, mask_kind(causal))
+           d, code, mask_kind(causal))
     n = _FWD_WS_BYTES.get(key)
     if n is None:
-        n = int(load().fa_fwd_ex_workspace_bytes(B, H, Hkv, N, Nk, d, mask_kind(causal)))
+        n = int(load().fa_fwd_ex_workspace_bytes(B, H, Hkv, N, Nk, d, code, mask_kind(causal)))
         _FWD_WS_BYTES[key] = n
     return n
 
@@ -199,21 +213,21 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
         ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward of q [B, H, Nq, d] over k, v [B, Hkv, Nk, d]. Returns (O, lse).
 
-    bfloat16: fa_fwd when Hkv = H, Nq = Nk and split is False, else fa_fwd_ex.
-    float32: fa_fwd_f32, or fa_fwd_f32_ex for other shapes. With split=True
-    (bfloat16 only) fa_fwd_ex may split the key range of heavy query tiles
-    over several workgroups, using `workspace` (a uint8 device tensor whose
-    first 64 KiB are zero, of at least split_workspace_bytes(...) bytes) or,
-    if None, a per-device cached one.
+    bfloat16 with Hkv = H, Nq = Nk and split False calls fa_fwd; float32 with
+    Hkv = H and Nq = Nk calls fa_fwd_f32; every other case (float16, grouped
+    K/V heads, Nq != Nk, split) calls fa_fwd_ex. With split=True (16-bit
+    types) fa_fwd_ex may split the key range of heavy query tiles over several
+    workgroups, using `workspace` (a uint8 device tensor whose first 64 KiB
+    are zero, of at least split_workspace_bytes(...) bytes) or, if None, a
+    per-device cached one.
     """
     B, H, Hkv, Nq, Nk, d = _check_qkv(q, k, v)
     plain = (Hkv == H and Nq == Nk)
+    code = dtype_code(q.dtype)
     if scale is None:
         scale = default_scale(d)
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("q, k, v must be bfloat16 or float32")
-    if split and q.dtype != torch.bfloat16:
-        raise ValueError("split-KV is a bfloat16 path")
+    if split and code == FA_DTYPE_F32:
+        raise ValueError("split-KV is a 16-bit path")
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
@@ -230,22 +244,17 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
     tensors = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse))
     with torch.cuda.device(q.device):
         stream = _stream(q.device)
-        if q.dtype == torch.float32:
-            if plain:
-                fn_name = "fa_fwd_f32"
-                st = lib.fa_fwd_f32(*tensors, B, H, Nq, d, float(scale), mask, kvp, stream)
-            else:
-                fn_name = "fa_fwd_f32_ex"
-                st = lib.fa_fwd_f32_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask, kvp,
-                                       stream)
-        elif plain and not split:
+        if code == FA_DTYPE_F32 and plain:
+            fn_name = "fa_fwd_f32"
+            st = lib.fa_fwd_f32(*tensors, B, H, Nq, d, float(scale), mask, kvp, stream)
+        elif code == FA_DTYPE_BF16 and plain and not split:
             fn_name = "fa_fwd"
             st = lib.fa_fwd(*tensors, B, H, Nq, d, float(scale), mask, kvp, stream)
         else:
             fn_name = "fa_fwd_ex"
             ws_ptr, ws_bytes = None, 0
             if split and workspace is None:
-                need = split_workspace_bytes(B, H, Nq, d, causal, Hkv, Nk)
+                need = split_workspace_bytes(B, H, Nq, d, causal, Hkv, Nk, q.dtype)
                 if need > 0:
                     workspace = _fwd_workspace(q.device, need)
             if split and workspace is not None:
@@ -253,8 +262,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
                     raise ValueError("workspace must be a contiguous tensor on q's device")
                 ws_ptr = workspace.data_ptr()
                 ws_bytes = workspace.numel() * workspace.element_size()
-            st = lib.fa_fwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask, kvp, ws_ptr,
-                               ws_bytes, stream)
+            st = lib.fa_fwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, code, float(scale), mask, kvp,
+                               ws_ptr, ws_bytes, stream)
     _check(fn_name, st)
     return out, lse
 
@@ -269,11 +278,12 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward (bfloat16): fa_bwd when Hkv = H and Nq = Nk, else fa_bwd_ex.
-    Returns (dQ [B, H, Nq, d], dK, dV [B, Hkv, Nk, d])."""
+    """Backward (bfloat16 or float16): fa_bwd for bfloat16 with Hkv = H and
+    Nq = Nk, else fa_bwd_ex. Returns (dQ [B, H, Nq, d], dK, dV [B, Hkv, Nk, d])."""
     B, H, Hkv, Nq, Nk, d = _check_qkv(q, k, v)
-    if q.dtype != torch.bfloat16:
-        raise ValueError("the backward takes bfloat16 tensors")
+    code = dtype_code(q.dtype)
+    if code == FA_DTYPE_F32:
+        raise ValueError("the backward takes bfloat16 or float16 tensors")
     for name, t in (("o", o), ("dout", dout)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must match q")
@@ -297,12 +307,12 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                _ptr(dv), _ptr(workspace))
     with torch.cuda.device(q.device):
         stream = _stream(q.device)
-        if Hkv == H and Nq == Nk:
+        if code == FA_DTYPE_BF16 and Hkv == H and Nq == Nk:
             fn_name = "fa_bwd"
             st = lib.fa_bwd(*tensors, B, H, Nq, d, float(scale), mask_kind(causal), kvp, stream)
         else:
             fn_name = "fa_bwd_ex"
-            st = lib.fa_bwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, float(scale), mask_kind(causal),
-                               kvp, stream)
+            st = lib.fa_bwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, code, float(scale),
+                               mask_kind(causal), kvp, stream)
     _check(fn_name, st)
     return dq, dk, dv

@@ -21,12 +21,12 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
 
-# Per-source extra flags. The bf16 forward keeps its MFMA accumulators in
+# Per-source extra flags. The 16-bit forward keeps its MFMA accumulators in
 # VGPRs (its rare rescale multiplies them with VALU instructions, which cannot
-# read AGPRs); Q operands are placed in AGPRs explicitly in the source.
-EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# read AGPRs).
+EXTRA = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 COMMON = [

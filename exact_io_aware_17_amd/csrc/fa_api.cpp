@@ -35,6 +35,10 @@ int check_common(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int 
   return FA_OK;
 }
 
+bool valid_dtype(int dtype) {
+  return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_F32;
+}
+
 float scale_log2(float scale) {
   return (float)((double)scale * 1.4426950408889634073599246810019);
 }
@@ -50,13 +54,15 @@ const fa::FwdPlan& no_plan() {
 }
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-               int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
-               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream,
-               size_t elem, bool f32) {
+               int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
+               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!workspace && workspace_bytes) return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
   int st = check_common(B, H, Hkv, Nq, Nk, d, scale, mask_kind);
   if (st != FA_OK) return st;
+  const bool f32 = (dtype == FA_DTYPE_F32);
+  const size_t elem = f32 ? 4 : 2;
   const size_t qbytes = (size_t)B * H * Nq * d * elem;    // q, o
   const size_t kbytes = (size_t)B * Hkv * Nk * d * elem;  // k, v
   const size_t lbytes = (size_t)B * H * Nq * sizeof(float);
@@ -90,6 +96,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.N = Nq;
   p.Nk = Nk;
   p.d = d;
+  p.dtype = f32 ? fa::DTYPE_F32 : (dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16);
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind != FA_MASK_NONE);
@@ -106,7 +113,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   if (workspace) {
     const int BH = B * H;
     int cus = 0, occ = 0;
-    fa::fwd_occupancy(d, p.causal != 0, &cus, &occ);
+    fa::fwd_occupancy(d, p.causal != 0, p.dtype, &cus, &occ);
     const fa::FwdPlan& cand = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, Nq, d);
     if (cand.nitems > 0 && workspace_bytes >= w.total) {
@@ -117,18 +124,20 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
       p.part_o = (float*)((char*)workspace + w.part_o);
     }
   }
-  hipError_t e = fa::launch_fwd_bf16(p, *plan, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd(p, *plan, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
-               int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+               int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
   int st = check_common(B, H, Hkv, Nq, Nk, d, scale, mask_kind);
   if (st != FA_OK) return st;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   const size_t qbytes = (size_t)B * H * Nq * d * 2;    // q, o, dout, dq
   const size_t kbytes = (size_t)B * Hkv * Nk * d * 2;  // k, v, dk, dv
   const size_t lbytes = (size_t)B * H * Nq * sizeof(float);
@@ -167,11 +176,12 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   p.N = Nq;
   p.Nk = Nk;
   p.d = d;
+  p.dtype = (dtype == FA_DTYPE_F16) ? fa::DTYPE_F16 : fa::DTYPE_BF16;
   p.scale = scale;
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind != FA_MASK_NONE);
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
-  hipError_t e = fa::launch_bwd_bf16(p, (hipStream_t)stream);
+  hipError_t e = fa::launch_bwd(p, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -198,37 +208,32 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, scale, mask_kind, kv_lens, nullptr, 0,
-                    stream, 2, false);
+  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, FA_DTYPE_BF16, scale, mask_kind, kv_lens,
+                    nullptr, 0, stream);
 }
 
-size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int mask_kind) {
+size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype,
+                                 int mask_kind) {
   if (check_common(B, H, Hkv, Nq, Nk, d, 1.f, mask_kind) != FA_OK) return 0;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return 0;  // fp32: never split
   const bool causal = (mask_kind != FA_MASK_NONE);
   int cus = 0, occ = 0;
-  fa::fwd_occupancy(d, causal, &cus, &occ);
+  fa::fwd_occupancy(d, causal, dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16, &cus, &occ);
   const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, cus, occ);
   return fa::fwd_workspace_layout(plan, B * H, Nq, d).total;
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, mask_kind, kv_lens, workspace,
-                    workspace_bytes, stream, 2, false);
+  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, dtype, scale, mask_kind, kv_lens,
+                    workspace, workspace_bytes, stream);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, scale, mask_kind, kv_lens, nullptr, 0,
-                    stream, 4, true);
-}
-
-int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse, int B,
-                  int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
-                  const int32_t* kv_lens, void* stream) {
-  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, mask_kind, kv_lens, nullptr, 0,
-                    stream, 4, true);
+  return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, FA_DTYPE_F32, scale, mask_kind, kv_lens,
+                    nullptr, 0, stream);
 }
 
 int fa_fwd_schedule(int Nq, int Nk, int BH, int mask_kind, int cus, int occ, uint32_t* items,
@@ -253,16 +258,16 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
-  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H, N, N, d, scale,
-                    mask_kind, kv_lens, stream);
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H, N, N, d, FA_DTYPE_BF16,
+                    scale, mask_kind, kv_lens, stream);
 }
 
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
-              int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
+              int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
               const int32_t* kv_lens, void* stream) {
-  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk, d, scale,
-                    mask_kind, kv_lens, stream);
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk, d, dtype,
+                    scale, mask_kind, kv_lens, stream);
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-// Exact attention backward for gfx950: P recomputed from the saved logsumexp.
+// Exact attention backward for gfx950 (bf16 or fp16 tensors, fp32
+// accumulation): P recomputed from the saved logsumexp.
 //
 // The pages say only that the backward pass recomputes S and P from Q, K, V
 // instead of storing them ("Question bank", the recomputation answers); the
@@ -57,8 +58,6 @@ __device__ __forceinline__ int tswz(int row) {
   }
 }
 
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Tile-major work order: workgroup id w takes tile rank w / (B*H) of head
 // w % (B*H). Workgroups are dispatched in id order, round-robin over the 8
@@ -68,8 +67,9 @@ __device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
 __device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
 
 // ---- per row: D_i = sum_c dO_ic O_ic and lse_i * log2(e) ----
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  typedef Elem<T> E;
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;
   const long long rows = (long long)p.B * p.H * p.N;
@@ -77,12 +77,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 a = *(const u32x4*)((const __bf16*)p.o + row * D + c * 8);
-    const u32x4 g = *(const u32x4*)((const __bf16*)p.dout + row * D + c * 8);
+    const u32x4 a = *(const u32x4*)((const T*)p.o + row * D + c * 8);
+    const u32x4 g = *(const u32x4*)((const T*)p.dout + row * D + c * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf_lo(a[e]), bf_lo(g[e]), acc);
-      acc = fmaf(bf_hi(a[e]), bf_hi(g[e]), acc);
+      acc = fmaf(E::lo(a[e]), E::lo(g[e]), acc);
+      acc = fmaf(E::hi(a[e]), E::hi(g[e]), acc);
     }
   }
 #pragma unroll
@@ -94,11 +94,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// DMA of rows [r0, r0 + BS) of a row-major [N, D] bf16 matrix into an LDS tile
+// DMA of rows [r0, r0 + BS) of a row-major [N, D] 16-bit matrix into an LDS tile
 // (rows past N repeat row N-1; they are masked by the callers).
 template <int D>
-__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ X, int r0, int N, char* dst,
+__device__ __forceinline__ void issue_tile(const void* __restrict__ Xv, int r0, int N, char* dst,
                                            int wave, int lane) {
+  const unsigned short* __restrict__ X = (const unsigned short*)Xv;
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int DMA_PER_TILE = BS * ROWB / 1024;
@@ -143,33 +144,35 @@ struct TileOffsets {
 };
 
 // Transposed A operand (d rows dt*32.., streamed-row chunk kc) of a tile.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const char* tile, const TileOffsets<D>& o, int dt,
+template <typename X8, int D>
+__device__ __forceinline__ X8 tr_operand(const char* tile, const TileOffsets<D>& o, int dt,
                                              int kc) {
   constexpr int ROWB = D * 2;
   const i16x4 lo = lds_read_tr16(tile + kc * 16 * ROWB + o.toff[dt][0]);
   const i16x4 hi = lds_read_tr16(tile + kc * 16 * ROWB + o.toff[dt][1]);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(X8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Store a transposed accumulator (lane = one output row, registers = D
-// columns in groups of 4) as bf16, times `mul`.
-template <int D>
-__device__ __forceinline__ void store_rowT(__bf16* dst, const f32x16* acc, float mul, int h) {
+// columns in groups of 4) as T, times `mul`.
+template <typename T, int D>
+__device__ __forceinline__ void store_rowT(T* dst, const f32x16* acc, float mul, int h) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x2 w;
-      w[0] = pack_bf16x2(acc[t][4 * g] * mul, acc[t][4 * g + 1] * mul);
-      w[1] = pack_bf16x2(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
+      w[0] = Elem<T>::pack(acc[t][4 * g] * mul, acc[t][4 * g + 1] * mul);
+      w[1] = Elem<T>::pack(acc[t][4 * g + 2] * mul, acc[t][4 * g + 3] * mul);
       *(u32x2*)(dst + t * 32 + 8 * g + 4 * h) = w;
     }
 }
 
 // ---- dQ: one workgroup per 128 query rows ----
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdParams p) {
+  typedef Elem<T> E;
+  typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(1024))) char kbuf[2][TB];  // K block, row-major
@@ -194,19 +197,19 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
 
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
-  const __bf16* Q = (const __bf16*)p.q + head;
-  const __bf16* K = (const __bf16*)p.k + kvhead;
-  const __bf16* V = (const __bf16*)p.v + kvhead;
-  const __bf16* dO = (const __bf16*)p.dout + head;
+  const T* Q = (const T*)p.q + head;
+  const T* K = (const T*)p.k + kvhead;
+  const T* V = (const T*)p.v + kvhead;
+  const T* dO = (const T*)p.dout + head;
 
   const int qa = q0 + wave * 32;
   const int qrow = qa + n;
   const int qrow_c = min(qrow, N - 1);
-  bf16x8 qf[DC], of[DC];
+  x8 qf[DC], of[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    qf[c] = *(const bf16x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
-    of[c] = *(const bf16x8*)(dO + (size_t)qrow_c * D + 16 * c + 8 * h);
+    qf[c] = *(const x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
+    of[c] = *(const x8*)(dO + (size_t)qrow_c * D + 16 * c + 8 * h);
   }
   const float lse2 = p.lse2[(size_t)bh * N + qrow_c];
   const float dl = p.delta[(size_t)bh * N + qrow_c];
@@ -239,15 +242,15 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
     zero(dp);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      s = mfma32(*(const bf16x8*)(ks + off.roff[c]), qf[c], s);
-      dp = mfma32(*(const bf16x8*)(vs + off.roff[c]), of[c], dp);
+      s = E::mfma(*(const x8*)(ks + off.roff[c]), qf[c], s);
+      dp = E::mfma(*(const x8*)(vs + off.roff[c]), of[c], dp);
     }
     __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa + shift);
     int lim = kvlen - 1;  // key visible iff key <= lim
     if (CAUSAL) lim = min(lim, qrow + shift);
     lim -= key0 + 4 * h;
-    bf16x8 df[2];
+    x8 df[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       u32x4 w;
@@ -261,26 +264,28 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
           if (need_mask && 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
           v2[u] = pv * (dp[r] - dl);  // dS^T
         }
-        w[e] = pack_bf16x2(v2[0], v2[1]);
+        w[e] = E::pack(v2[0], v2[1]);
       }
-      df[kc] = __builtin_bit_cast(bf16x8, w);
+      df[kc] = __builtin_bit_cast(x8, w);
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) acc[dt] = mfma32(tr_operand<D>(ks, off, dt, kc), df[kc], acc[dt]);
+      for (int kc = 0; kc < 2; ++kc) acc[dt] = E::mfma(tr_operand<x8, D>(ks, off, dt, kc), df[kc], acc[dt]);
     __builtin_amdgcn_s_setprio(0);
   }
   wait_vmem();
 
-  if (qrow < N) store_rowT<D>((__bf16*)p.dq + head + (size_t)qrow * D, acc, p.scale, h);
+  if (qrow < N) store_rowT<T, D>((T*)p.dq + head + (size_t)qrow * D, acc, p.scale, h);
 }
 
 // ---- dK, dV: one workgroup per 128 keys of a K/V head, summed over the
 // query heads that share it ----
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void bwd_dkdv_kernel(BwdParams p) {
+  typedef Elem<T> E;
+  typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
   constexpr int DC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(1024))) char qbuf[2][TB];  // Q block, row-major
@@ -301,17 +306,17 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
 
   const size_t kvhead = (size_t)bkv * Nk * D;
   const size_t qhead0 = (size_t)bkv * G;  // first query head of the group (b * H + hk * G)
-  const __bf16* K = (const __bf16*)p.k + kvhead;
-  const __bf16* V = (const __bf16*)p.v + kvhead;
+  const T* K = (const T*)p.k + kvhead;
+  const T* V = (const T*)p.v + kvhead;
 
   const int kw0 = kb0 + wave * 32;
   const int key = kw0 + n;
   const int key_c = min(key, Nk - 1);
-  bf16x8 kf[DC], vf[DC];
+  x8 kf[DC], vf[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    kf[c] = *(const bf16x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
-    vf[c] = *(const bf16x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
+    kf[c] = *(const x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
+    vf[c] = *(const x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
   }
   __builtin_amdgcn_sched_barrier(0);
   const float scl = p.scale_log2;
@@ -334,8 +339,8 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
     if (u >= nsteps) return;
     const int g = u / nq, i = qstart + u % nq;
     const size_t qh = qhead0 + g;
-    issue_tile<D>((const __bf16*)p.q + qh * N * D, i * BS, N, qbuf[u & 1], wave, lane);
-    issue_tile<D>((const __bf16*)p.dout + qh * N * D, i * BS, N, obuf[u & 1], wave, lane);
+    issue_tile<D>((const T*)p.q + qh * N * D, i * BS, N, qbuf[u & 1], wave, lane);
+    issue_tile<D>((const T*)p.dout + qh * N * D, i * BS, N, obuf[u & 1], wave, lane);
     if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
       const int qi = min(i * BS + (lane & 31), N - 1);
       const float* src = ((lane < 32) ? p.lse2 : p.delta) + qh * N + qi;
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
     f32x16 s;
     zero(s);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) s = mfma32(*(const bf16x8*)(qs + off.roff[c]), kf[c], s);
+    for (int c = 0; c < DC; ++c) s = E::mfma(*(const x8*)(qs + off.roff[c]), kf[c], s);
     __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0 + shift);
 #pragma unroll
@@ -378,25 +383,25 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
         s[r] = pr;  // P, fp32
       }
     }
-    bf16x8 pf[2];
+    x8 pf[2];
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[8 * qc + 2 * e], s[8 * qc + 2 * e + 1]);
-      pf[qc] = __builtin_bit_cast(bf16x8, w);
+      for (int e = 0; e < 4; ++e) w[e] = E::pack(s[8 * qc + 2 * e], s[8 * qc + 2 * e + 1]);
+      pf[qc] = __builtin_bit_cast(x8, w);
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) dva[dt] = mfma32(tr_operand<D>(os, off, dt, qc), pf[qc], dva[dt]);
+      for (int qc = 0; qc < 2; ++qc) dva[dt] = E::mfma(tr_operand<x8, D>(os, off, dt, qc), pf[qc], dva[dt]);
     f32x16 dp;
     zero(dp);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) dp = mfma32(*(const bf16x8*)(os + off.roff[c]), vf[c], dp);
+    for (int c = 0; c < DC; ++c) dp = E::mfma(*(const x8*)(os + off.roff[c]), vf[c], dp);
     __builtin_amdgcn_s_setprio(0);
-    bf16x8 df[2];
+    x8 df[2];
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
       u32x4 w;
@@ -407,27 +412,27 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 4 * g + 2 * e;
-          w[2 * g2 + e] = pack_bf16x2(s[r] * (dp[r] - d4[2 * e]), s[r + 1] * (dp[r + 1] - d4[2 * e + 1]));
+          w[2 * g2 + e] = E::pack(s[r] * (dp[r] - d4[2 * e]), s[r + 1] * (dp[r + 1] - d4[2 * e + 1]));
         }
       }
-      df[qc] = __builtin_bit_cast(bf16x8, w);
+      df[qc] = __builtin_bit_cast(x8, w);
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) dka[dt] = mfma32(tr_operand<D>(qs, off, dt, qc), df[qc], dka[dt]);
+      for (int qc = 0; qc < 2; ++qc) dka[dt] = E::mfma(tr_operand<x8, D>(qs, off, dt, qc), df[qc], dka[dt]);
     __builtin_amdgcn_s_setprio(0);
   }
   wait_vmem();
 
   if (key < Nk) {
-    store_rowT<D>((__bf16*)p.dk + kvhead + (size_t)key * D, dka, p.scale, h);
-    store_rowT<D>((__bf16*)p.dv + kvhead + (size_t)key * D, dva, 1.f, h);
+    store_rowT<T, D>((T*)p.dk + kvhead + (size_t)key * D, dka, p.scale, h);
+    store_rowT<T, D>((T*)p.dv + kvhead + (size_t)key * D, dva, 1.f, h);
   }
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
   const long long rpb = 256 / (D / 8);
@@ -435,16 +440,17 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);     // dQ: query tiles
   const long long g2 = (long long)p.B * p.Hkv * ((p.Nk + BT - 1) / BT);  // dK, dV: key tiles
   if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
   if (p.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)g2), dim3(NWB * 64), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3((unsigned)g2), dim3(NWB * 64), 0,
+                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
                        p);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)g2), dim3(NWB * 64), 0, stream,
-                       p);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
-                       p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3((unsigned)g2), dim3(NWB * 64), 0,
+                       stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0,
+                       stream, p);
   }
   return hipGetLastError();
 }
@@ -458,9 +464,14 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * one;  // D, then lse*log2(e)
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  if (p.d == 128) return launch_d<128>(p, stream);
-  if (p.d == 64) return launch_d<64>(p, stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  if (p.dtype == DTYPE_BF16) {
+    if (p.d == 128) return launch_d<__bf16, 128>(p, stream);
+    if (p.d == 64) return launch_d<__bf16, 64>(p, stream);
+  } else if (p.dtype == DTYPE_F16) {
+    if (p.d == 128) return launch_d<_Float16, 128>(p, stream);
+    if (p.d == 64) return launch_d<_Float16, 64>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

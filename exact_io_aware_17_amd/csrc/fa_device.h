@@ -8,6 +8,8 @@ namespace dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -100,6 +102,52 @@ __device__ __forceinline__ float add_bf16_pair(unsigned w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
+
+// Sum of a packed pair of fp16 values added to an fp32 accumulator (v_dot2_f32_f16).
+__device__ __forceinline__ float add_f16_pair(unsigned w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u),
+                                acc, false);
+}
+
+// The 16-bit input element types: bf16 and fp16 share every kernel; only the
+// matrix instruction, the rounding of fp32 values to the element type
+// (round-to-nearest-even) and the pair sum differ.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  typedef bf16x8 x8;
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ float add_pair(unsigned w, float acc) {
+    return add_bf16_pair(w, acc);
+  }
+  static __device__ __forceinline__ float lo(unsigned w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+};
+template <>
+struct Elem<_Float16> {
+  typedef f16x8 x8;
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack(float a, float b) {
+    f32x2 v = {a, b};
+    f16x2 r = __builtin_convertvector(v, f16x2);
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float add_pair(unsigned w, float acc) {
+    return add_f16_pair(w, acc);
+  }
+  static __device__ __forceinline__ float lo(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(unsigned w) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+  }
+};
 
 // Raw buffer resource over `base` (byte offsets up to 2^31 - 1, no bounds
 // checking beyond that; the caller keeps offsets inside its allocation).

@@ -1,4 +1,5 @@
-// Exact attention forward for gfx950: bf16 matrix cores, fp32 online softmax.
+// Exact attention forward for gfx950: bf16 or fp16 matrix cores, fp32 online
+// softmax.
 //
 // One workgroup of NW = 4 waves owns BM = 128 query rows of one (batch, head)
 // and streams the visible keys in blocks of BN keys through LDS, carrying per
@@ -9,13 +10,14 @@
 // memory.
 //
 // Layout (each wave owns 32 queries, one per lane pair):
-//  * Scores are produced transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA:
+//  * Scores are produced transposed, S^T = K Q^T, with the 32x32x16 MFMA of
+//    the input type (bf16 or fp16):
 //    A = a 32-key x 16-dim slice of K (LDS), B = the wave's Q^T slice (held in
 //    registers for the whole kernel). In the 32x32 accumulator lane l holds
 //    query (l % 32) and 16 keys, so row max and row sum are in-lane
 //    reductions plus one exchange between the two lane halves.
 //  * The output is accumulated transposed too, O^T += V^T P^T. B = P^T comes
-//    straight from the score registers after bf16 rounding; the contraction
+//    straight from the score registers after rounding to the input type; the contraction
 //    slots of the A operand are assigned to keys in the order the accumulator
 //    holds them (bits 2 and 3 of the key index swapped), which the contraction
 //    permits. A = V^T is read from the row-major V tile with the gfx950
@@ -36,7 +38,7 @@
 //    reference gives the same O = acc / l and lse = m + ln l exactly, and the
 //    lag bound keeps every exponential below 2^TAU.
 //  * Exponentials are base 2 (v_exp_f32) with scale*log2(e) folded into one
-//    FMA. Two row sums are kept: O is divided by the sum of the bf16-rounded
+//    FMA. Two row sums are kept: O is divided by the sum of the rounded
 //    weights that P V actually used (each output row is then a convex
 //    combination of V rows even where one weight dominates), and the
 //    logsumexp uses the sum of the fp32 probabilities (fp32 accuracy for the
@@ -87,8 +89,10 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 #define FA_FWD_WG_PER_CU 3
 #endif
 
-template <int D, int BN, int STAGES, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(FwdParams p, FwdPlan plan) {
+template <typename T, int D, int BN, int STAGES, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_kernel(FwdParams p, FwdPlan plan) {
+  typedef Elem<T> E;
+  typedef typename E::x8 x8;
   constexpr int ROWB = D * 2;                 // bytes per K/V row
   constexpr int TILE = BN * ROWB;             // bytes per K or V tile
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
@@ -155,17 +159,17 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 
   const size_t head = (size_t)bh * N * D;  // Q, O rows of this head
   const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
-  const __bf16* __restrict__ Q = (const __bf16*)p.q + head;
-  const __bf16* __restrict__ K = (const __bf16*)p.k + kvhead;
-  const __bf16* __restrict__ V = (const __bf16*)p.v + kvhead;
+  const T* __restrict__ Q = (const T*)p.q + head;
+  const T* __restrict__ K = (const T*)p.k + kvhead;
+  const T* __restrict__ V = (const T*)p.v + kvhead;
 
   // ---- Q^T fragments: lane (n, h) holds query qrow, dims 16c + 8h .. +8 ----
-  bf16x8 qf[DC];
+  x8 qf[DC];
   {
     const int qrow_c = min(qrow, N - 1);
 #pragma unroll
     for (int c = 0; c < DC; ++c)
-      qf[c] = *(const bf16x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
+      qf[c] = *(const x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
 #pragma unroll
   for (int c = 0; c < DC; ++c) koff[c] = n * ROWB + (((2 * c + h) ^ kswz<D>(n)) * 16);
   // V^T transpose reads: row 16*kc + 8r + 4h + (lane%16)/4, column
-  // dt*32 + 16*((lane/16)%2) + 4*(lane%4) (four bf16 = 8 bytes). The swizzle
+  // dt*32 + 16*((lane/16)%2) + 4*(lane%4) (four elements = 8 bytes). The swizzle
   // depends only on the row's low bits, which 16*kc + 8r leaves unchanged.
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vrow = 4 * h + ((lane & 15) >> 2);
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
   float m_run = NEG_INF;  // reference max (scaled log2 units)
   float l_run = 0.f;      // this lane's share of sum p (fp32)
-  float l_bf = 0.f;       // the same over the bf16-rounded p used by P V
+  float l_bf = 0.f;       // the same over the rounded (16-bit) p used by P V
   const float scl = p.scale_log2;
 
   // One key block: the stage (LDS buffer) is a compile-time constant, so
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     for (int c = 0; c < DC; ++c)
 #pragma unroll
       for (int t = 0; t < KT; ++t)
-        s[t] = mfma32(*(const bf16x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
+        s[t] = E::mfma(*(const x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
 
     __builtin_amdgcn_s_setprio(0);
     // ---- mask (only blocks that straddle the diagonal or kv_len) ----
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
     // the only case that needs the block max: then the reference moves to
     // the row's block max if that lies more than TAU above it (rescaling the
     // accumulators once), and the block's p are recomputed.
-    bf16x8 pf[KC];
+    x8 pf[KC];
     float rs, lbf_blk;
     auto probabilities = [&](float m_use) {
       rs = 0.f;
@@ -299,11 +303,11 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
           const int r = 8 * (kc & 1) + 2 * e;
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], scl, -m_use));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r + 1], scl, -m_use));
-          w[e] = pack_bf16x2(p0, p1);
+          w[e] = E::pack(p0, p1);
           rs += p0 + p1;
-          lbf_blk = add_bf16_pair(w[e], lbf_blk);
+          lbf_blk = E::add_pair(w[e], lbf_blk);
         }
-        pf[kc] = __builtin_bit_cast(bf16x8, w);
+        pf[kc] = __builtin_bit_cast(x8, w);
       }
     };
     probabilities(m_run);
@@ -337,9 +341,8 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
       for (int kc = 0; kc < KC; ++kc) {
         const i16x4 lo = lds_read_tr16(vs + kc * 16 * ROWB + voff[dt]);
         const i16x4 hi = lds_read_tr16(vs + (kc * 16 + 8) * ROWB + voff[dt]);
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[dt] = mfma32(a, pf[kc], acc[dt]);
+        const x8 a = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = E::mfma(a, pf[kc], acc[dt]);
       }
   };
 
@@ -422,14 +425,14 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   const bool empty = (l_tot == 0.f);
   const float inv = empty ? 0.f : 1.f / l_o;
   if (qrow < N) {
-    __bf16* O = (__bf16*)p.o + head + (size_t)qrow * D;
+    T* O = (T*)p.o + head + (size_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack_bf16x2(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        w[0] = E::pack(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
+        w[1] = E::pack(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
         *(u32x2*)(O + dt * 32 + 8 * g + 4 * h) = w;
       }
     if (h == 0 && p.lse) {
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_bf16_kernel(Fwd
   }
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
   constexpr int BN = FA_FWD_BN, ST = FA_FWD_STAGES;
   static_assert(BN == FWD_BN, "the host planner counts blocks of FWD_BN keys");
@@ -447,48 +450,60 @@ hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream)
   const long long grid = (long long)p.B * p.H * items;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, ST, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
                        stream, p, plan);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, ST, false>), dim3((unsigned)grid), dim3(NW * 64),
-                       0, stream, p, plan);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, ST, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       stream, p, plan);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 int occupancy() {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&fwd_bf16_kernel<D, FA_FWD_BN, FA_FWD_STAGES, CAUSAL>),
+          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, FA_FWD_BN, FA_FWD_STAGES, CAUSAL>),
           NW * 64, 0) != hipSuccess)
     return 0;
   return per;
 }
 
+template <typename T>
+int occupancy_of(int d, bool causal) {
+  if (d == 128) return causal ? occupancy<T, 128, true>() : occupancy<T, 128, false>();
+  if (d == 64) return causal ? occupancy<T, 64, true>() : occupancy<T, 64, false>();
+  return 0;
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-  if (p.d == 128) return launch_d<128>(p, plan, stream);
-  if (p.d == 64) return launch_d<64>(p, plan, stream);
+hipError_t launch_fwd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
+  if (p.dtype == DTYPE_BF16) {
+    if (p.d == 128) return launch_d<__bf16, 128>(p, plan, stream);
+    if (p.d == 64) return launch_d<__bf16, 64>(p, plan, stream);
+  } else if (p.dtype == DTYPE_F16) {
+    if (p.d == 128) return launch_d<_Float16, 128>(p, plan, stream);
+    if (p.d == 64) return launch_d<_Float16, 64>(p, plan, stream);
+  }
   return hipErrorInvalidValue;
 }
 
-void fwd_occupancy(int d, bool causal, int* cus_out, int* occ_out) {
+void fwd_occupancy(int d, bool causal, int dtype, int* cus_out, int* occ_out) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, bool>, std::pair<int, int>> cache;
+  static std::map<std::tuple<int, int, bool, int>, std::pair<int, int>> cache;
   *cus_out = 0;
   *occ_out = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_tuple(dev, d, causal);
+  const auto key = std::make_tuple(dev, d, causal, dtype);
   auto it = cache.find(key);
   if (it == cache.end()) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 0;
-    if (d == 128) per = causal ? occupancy<128, true>() : occupancy<128, false>();
-    if (d == 64) per = causal ? occupancy<64, true>() : occupancy<64, false>();
+    if (dtype == DTYPE_BF16) per = occupancy_of<__bf16>(d, causal);
+    if (dtype == DTYPE_F16) per = occupancy_of<_Float16>(d, causal);
     if (cus <= 0 || per <= 0) cus = per = 0;
     it = cache.emplace(key, std::make_pair(cus, per)).first;
   }

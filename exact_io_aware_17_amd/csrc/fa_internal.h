@@ -7,6 +7,9 @@
 
 namespace fa {
 
+// Element types of q, k, v, o (and of the gradients).
+enum { DTYPE_BF16 = 0, DTYPE_F16 = 1, DTYPE_F32 = 2 };
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -16,6 +19,7 @@ struct FwdParams {
   const int32_t* kv_lens;  // may be null
   int B, H, N, d;          // N: query rows per head
   int Hkv, Nk;             // K/V heads (a divisor of H) and key rows per head
+  int dtype;               // DTYPE_*
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
   int causal;              // key j visible to query i only if j <= i + Nk - N - diag
@@ -62,8 +66,8 @@ struct FwdWorkspace {
 };
 FwdWorkspace fwd_workspace_layout(const FwdPlan& plan, int BH, int N, int d);
 // Compute units of the current device and resident forward workgroups per
-// compute unit (both 0 if unknown).
-void fwd_occupancy(int d, bool causal, int* cus, int* occ);
+// compute unit for head dimension d and element type dtype (both 0 if unknown).
+void fwd_occupancy(int d, bool causal, int dtype, int* cus, int* occ);
 
 struct BwdParams {
   const void* q;
@@ -80,6 +84,7 @@ struct BwdParams {
   const int32_t* kv_lens;
   int B, H, N, d;          // N: query rows per head
   int Hkv, Nk;             // as FwdParams
+  int dtype;               // DTYPE_BF16 or DTYPE_F16
   float scale;
   float scale_log2;
   int causal;
@@ -87,9 +92,10 @@ struct BwdParams {
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().
-hipError_t launch_fwd_bf16(const FwdParams& p, const FwdPlan& plan, hipStream_t stream);
+// launch_fwd and launch_bwd take bf16 or fp16 tensors (p.dtype).
+hipError_t launch_fwd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 

@@ -8,7 +8,7 @@ fed from it without sharing any of their computation.
 Recipe (one CPU ``torch.Generator`` per workload, seed 17000 + workload id):
   randn float32 [B, H, N, d] drawn in the order Q, K, V (then dO when the
   workload has a backward), then the per-workload multiplier on Q, then the
-  cast to the workload dtype (round-to-nearest-even for bf16), then per-batch
+  cast to the workload dtype (round-to-nearest-even for bf16 and fp16), then per-batch
   key lengths when the workload is padded: [0, 1, then B-2 uniform draws on
   {0, ..., N}] from the same generator.
 """
@@ -29,7 +29,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str              # "f32" or "bf16"
+    dtype: str              # "f32", "bf16" or "f16"
     causal: object  # False, True (key j visible iff j <= i) or "strict" (iff j < i)
     q_mult: float = 1.0     # Q is multiplied by this before the cast
     padded: bool = False    # per-batch key lengths are drawn
@@ -46,7 +46,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[self.dtype]
 
     def describe(self) -> Dict:
         return {"workload": self.name, "B": self.B, "H": self.H, "N": self.N, "d": self.d,

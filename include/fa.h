@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_OK = 0,
@@ -71,6 +71,13 @@ typedef enum {
   FA_ERR_UNSUPPORTED = -2,
   FA_ERR_HIP = -3
 } fa_status;
+
+/* Element type of q, k, v, o (and dout, dq, dk, dv) in the _ex entry points. */
+typedef enum {
+  FA_DTYPE_BF16 = 0,  /* bfloat16; matrix products on bf16 MFMA, fp32 accumulation */
+  FA_DTYPE_F16 = 1,   /* IEEE half; fp16 MFMA, fp32 accumulation */
+  FA_DTYPE_F32 = 2    /* float32 throughout (forward only, no split) */
+} fa_dtype;
 
 typedef enum {
   FA_MASK_NONE = 0,          /* every key visible (subject to kv_lens) */
@@ -102,12 +109,14 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Bytes of workspace fa_fwd_ex needs for these sizes on the current device
  * to split key ranges; 0 when its plan does not split any tile (then no
- * workspace is needed), or for invalid arguments.
+ * workspace is needed), for FA_DTYPE_F32, or for invalid arguments.
  */
-size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int mask_kind);
+size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int dtype,
+                                 int mask_kind);
 
 /*
- * fa_fwd for grouped K/V heads (Hkv) and Nq != Nk (see the shapes and
+ * fa_fwd for any element type (dtype: FA_DTYPE_BF16, FA_DTYPE_F16 or
+ * FA_DTYPE_F32), grouped K/V heads (Hkv) and Nq != Nk (see the shapes and
  * visibility above), with optional split-KV: given a workspace, the key range
  * of the heaviest query tiles is split over several workgroups; each part
  * streams its share of the keys, stores its partial softmax state (row max,
@@ -118,7 +127,7 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
  * long rows, short decode queries over long caches) this spreads a tile over
  * several compute units. Same results as without the split up to rounding;
  * bitwise reproducible for a given device and shape.
- *   q, o      : [B, H, Nq, d] bfloat16;  k, v : [B, Hkv, Nk, d] bfloat16
+ *   q, o      : [B, H, Nq, d];  k, v : [B, Hkv, Nk, d]; all of type dtype
  *   lse       : [B, H, Nq] float32 or NULL
  *   kv_lens   : device int32 [B] valid key counts (clamped to [0, Nk]), or NULL
  *   workspace : device memory, or NULL with workspace_bytes = 0 (no split).
@@ -128,13 +137,17 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
  *               zero, for any later shape (the rest is scratch). Calls
  *               sharing a workspace must be ordered (same stream, or
  *               synchronised). It must not overlap any tensor argument.
- * Errors as fa_fwd, and FA_ERR_INVALID_ARG for workspace_bytes > 0 with a
- * NULL workspace, FA_ERR_UNSUPPORTED for a workspace not 16-byte aligned.
+ *               Not used with FA_DTYPE_F32.
+ * With FA_DTYPE_F16 the probabilities are rounded to fp16 (not bf16) before
+ * the P V product and O is written in fp16 (round-to-nearest-even).
+ * Errors as fa_fwd, and FA_ERR_INVALID_ARG for an unknown dtype or for
+ * workspace_bytes > 0 with a NULL workspace, FA_ERR_UNSUPPORTED for a
+ * workspace not 16-byte aligned.
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
-              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
-              const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
-              void* stream);
+              int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
+              int mask_kind, const int32_t* kv_lens, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 /*
  * The same contract with float32 q, k, v, o (float32 arithmetic throughout).
@@ -142,11 +155,6 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
-
-/* fa_fwd_f32 for grouped K/V heads and Nq != Nk (shapes as fa_fwd_ex). */
-int fa_fwd_f32_ex(const float* q, const float* k, const float* v, float* o, float* lse,
-                  int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
-                  const int32_t* kv_lens, void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (caller-allocated,
@@ -173,8 +181,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const int32_t* kv_lens, void* stream);
 
 /*
- * fa_bwd for grouped K/V heads and Nq != Nk (shapes as fa_fwd_ex):
- *   q, o, dout, dq : [B, H, Nq, d] bfloat16;  k, v, dk, dv : [B, Hkv, Nk, d]
+ * fa_bwd for bf16 or fp16 tensors (dtype FA_DTYPE_BF16 or FA_DTYPE_F16;
+ * FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED), grouped K/V heads and Nq != Nk
+ * (shapes as fa_fwd_ex):
+ *   q, o, dout, dq : [B, H, Nq, d];  k, v, dk, dv : [B, Hkv, Nk, d]
  *   lse            : [B, H, Nq] float32 from fa_fwd / fa_fwd_ex
  *   workspace      : fa_bwd_workspace_bytes(B, H, Nq, d) bytes
  * dK and dV of a K/V head are the sums over the H / Hkv query heads that
@@ -183,8 +193,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  */
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv, void* workspace,
-              int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int mask_kind,
-              const int32_t* kv_lens, void* stream);
+              int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
+              int mask_kind, const int32_t* kv_lens, void* stream);
 
 /*
  * Host-only view of fa_fwd_ex's work plan (no device call): for Nq query

@@ -48,21 +48,26 @@ def test_workspace_bytes():
     assert lib.fa_bwd_workspace_bytes(0, 16, 4096, 128) == 0
 
 
+# fa_fwd_ex under each element type: "fa_fwd_ex" is bf16, "fa_fwd_ex:1" fp16,
+# "fa_fwd_ex:2" fp32.
 def _fwd(fn="fa_fwd", q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ,
          B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None, ws=None, ws_bytes=0, Hkv=None,
-         Nk=None):
+         Nk=None, dtype=None):
     lib = _lib.load()
     Hkv = H if Hkv is None else Hkv
     Nk = N if Nk is None else Nk
-    if fn == "fa_fwd_ex":
-        return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, scale, mask, kv, ws, ws_bytes,
-                             None)
-    if fn == "fa_fwd_f32_ex":
-        return lib.fa_fwd_f32_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, scale, mask, kv, None)
+    if fn.startswith("fa_fwd_ex"):
+        code = int(fn.split(":")[1]) if ":" in fn else _lib.FA_DTYPE_BF16
+        code = code if dtype is None else dtype
+        return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, code, scale, mask, kv, ws,
+                             ws_bytes, None)
     return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, scale, mask, kv, None)
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_fwd_f32_ex"])
+EX = ["fa_fwd_ex", "fa_fwd_ex:1", "fa_fwd_ex:2"]
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"] + EX)
 def test_fwd_argument_errors(fn):
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
     assert _fwd(fn, q=None) == INV
@@ -85,7 +90,19 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, B=1 << 16, H=1 << 16, N=1) == UNS  # row count beyond 32-bit
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd_ex", "fa_fwd_f32_ex"])
+def test_dtype_argument_errors():
+    INV = _lib.FA_ERR_INVALID_ARG
+    assert _fwd("fa_fwd_ex", dtype=3) == INV
+    assert _fwd("fa_fwd_ex", dtype=-1) == INV
+    lib = _lib.load()
+    assert lib.fa_fwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, 3, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, 2, 1) == 0  # fp32: no split
+    # An fp32 q of [1, 1, 16, 64] is 4 KiB: o at q + 2 KiB overlaps it only when
+    # the element size is 4 bytes.
+    assert _fwd("fa_fwd_ex:2", o=A + 2048) == INV
+
+
+@pytest.mark.parametrize("fn", EX)
 def test_grouped_shape_argument_errors(fn):
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
     assert _fwd(fn, H=8, Hkv=0) == INV
@@ -98,7 +115,7 @@ def test_grouped_shape_argument_errors(fn):
     # of d=64 are 2 KiB in bf16), not from Nq = 4.
     assert _fwd(fn, N=4, Nk=16, o=A + SZ + 1024) == INV
     assert _fwd(fn, N=4, Nk=16, lse=A + 2 * SZ + 1024) == INV  # lse inside v
-    # k is [1, 2, 16, 64] bf16 = 4 KiB: o over its last 16 bytes.
+    # k is [1, 2, 16, 64] of 2-byte elements = 4 KiB: o over its last 16 bytes.
     assert _fwd(fn, H=8, Hkv=2, o=A + SZ + 2 * 16 * 64 * 2 - 16) == INV
 
 
@@ -114,11 +131,11 @@ def test_split_workspace_argument_errors():
 
 def test_split_workspace_bytes_invalid_sizes():
     lib = _lib.load()
-    assert lib.fa_fwd_ex_workspace_bytes(0, 16, 16, 4096, 4096, 128, 1) == 0
-    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 96, 1) == 0
-    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 128, 7) == 0
-    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 3, 4096, 4096, 128, 1) == 0
-    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 0, 128, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(0, 16, 16, 4096, 4096, 128, 0, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 96, 0, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 4096, 128, 0, 7) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 3, 4096, 4096, 128, 0, 1) == 0
+    assert lib.fa_fwd_ex_workspace_bytes(2, 16, 16, 4096, 0, 128, 0, 1) == 0
 
 
 def test_bwd_argument_errors():
@@ -154,10 +171,13 @@ def test_bwd_ex_argument_errors():
     INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
     base = [A + i * SZ for i in range(10)]
 
-    def call(ptrs=None, B=1, H=4, Hkv=2, Nq=16, Nk=32, d=64, scale=0.125, mask=1):
+    def call(ptrs=None, B=1, H=4, Hkv=2, Nq=16, Nk=32, d=64, scale=0.125, mask=1, dtype=0):
         p = list(base if ptrs is None else ptrs)
-        return lib.fa_bwd_ex(*p, B, H, Hkv, Nq, Nk, d, scale, mask, None, None)
+        return lib.fa_bwd_ex(*p, B, H, Hkv, Nq, Nk, d, dtype, scale, mask, None, None)
 
+    assert call(dtype=2) == UNS   # no fp32 backward
+    assert call(dtype=5) == INV
+    assert call(dtype=1, Hkv=3) == INV
     assert call(Hkv=3) == INV
     assert call(Hkv=0) == INV
     assert call(Nk=0) == INV
