@@ -38,7 +38,7 @@ KERNEL_SOURCES = [
     os.path.join(ROOT, "exact_io_aware_17_amd", "csrc", f)
     for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")
 ]
-FWD_KERNEL_TAG = "fwd_kernel<"  # the forward kernel's name in profiler output
+FWD_KERNEL_TAG = "fwd_kernel"  # in the forward kernel's name, mangled or not
 
 
 def kernel_source_hash() -> str:
