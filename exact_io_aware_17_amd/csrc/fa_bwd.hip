@@ -51,7 +51,8 @@ constexpr int BT = 32 * NWB;  // rows owned by a workgroup (queries in dq, keys 
 // each by the transpose reads, both spread evenly over the LDS banks.
 template <int D>
 __device__ __forceinline__ int tswz(int row) {
-  if constexpr (D == 128) {
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  if constexpr (D >= 128) {  // rows of 256 or 512 bytes: every row starts at bank 0
     return 4 * (row & 3) + ((row >> 2) & 3);
   } else {
     return ((row >> 1) & 1) | (((row >> 2) & 1) << 2) | (((row >> 3) & 1) << 1);
@@ -170,7 +171,7 @@ __device__ __forceinline__ void store_rowT(T* dst, const f32x16* acc, float mul,
 
 // ---- dQ: one workgroup per 128 query rows ----
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdParams p) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
@@ -282,8 +283,14 @@ __global__ __launch_bounds__(NWB * 64, FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdPara
 
 // ---- dK, dV: one workgroup per 128 keys of a K/V head, summed over the
 // query heads that share it ----
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void bwd_dkdv_kernel(BwdParams p) {
+// OUT selects the gradients computed: DKDV_V | DKDV_K in one pass, or (at
+// D = 256, where both sets of accumulators and both operand sets exceed the
+// register file) one of them per pass; the dV pass skips dP and dS.
+constexpr int DKDV_V = 1, DKDV_K = 2;
+constexpr int dkdv_waves_per_simd(int D) { return D == 256 ? 1 : (D == 128 ? FA_BWD_DKDV128_OCC : 2); }
+
+template <typename T, int D, bool CAUSAL, int OUT>
+__global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_kernel(BwdParams p) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
@@ -312,11 +319,11 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
   const int kw0 = kb0 + wave * 32;
   const int key = kw0 + n;
   const int key_c = min(key, Nk - 1);
-  x8 kf[DC], vf[DC];
+  x8 kf[DC], vf[(OUT & DKDV_K) ? DC : 1];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     kf[c] = *(const x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
-    vf[c] = *(const x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
+    if constexpr ((OUT & DKDV_K) != 0) vf[c] = *(const x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
   }
   __builtin_amdgcn_sched_barrier(0);
   const float scl = p.scale_log2;
@@ -392,10 +399,17 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
       pf[qc] = __builtin_bit_cast(x8, w);
     }
     __builtin_amdgcn_s_setprio(1);
+    if constexpr ((OUT & DKDV_V) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int qc = 0; qc < 2; ++qc) dva[dt] = E::mfma(tr_operand<x8, D>(os, off, dt, qc), pf[qc], dva[dt]);
+        for (int qc = 0; qc < 2; ++qc)
+          dva[dt] = E::mfma(tr_operand<x8, D>(os, off, dt, qc), pf[qc], dva[dt]);
+    }
+    if constexpr ((OUT & DKDV_K) == 0) {
+      __builtin_amdgcn_s_setprio(0);
+      continue;
+    }
     f32x16 dp;
     zero(dp);
 #pragma unroll
@@ -427,9 +441,26 @@ __global__ __launch_bounds__(NWB * 64, D == 128 ? FA_BWD_DKDV128_OCC : 2) void b
   wait_vmem();
 
   if (key < Nk) {
-    store_rowT<T, D>((T*)p.dk + kvhead + (size_t)key * D, dka, p.scale, h);
-    store_rowT<T, D>((T*)p.dv + kvhead + (size_t)key * D, dva, 1.f, h);
+    if constexpr ((OUT & DKDV_K) != 0)
+      store_rowT<T, D>((T*)p.dk + kvhead + (size_t)key * D, dka, p.scale, h);
+    if constexpr ((OUT & DKDV_V) != 0)
+      store_rowT<T, D>((T*)p.dv + kvhead + (size_t)key * D, dva, 1.f, h);
   }
+}
+
+template <typename T, int D, bool CAUSAL>
+void launch_grads(const BwdParams& p, long long g1, long long g2, hipStream_t stream) {
+  const dim3 blk(NWB * 64);
+  if constexpr (D == 256) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DKDV_V>), dim3((unsigned)g2), blk, 0, stream,
+                       p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DKDV_K>), dim3((unsigned)g2), blk, 0, stream,
+                       p);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DKDV_V | DKDV_K>), dim3((unsigned)g2), blk, 0,
+                       stream, p);
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g1), blk, 0, stream, p);
 }
 
 template <typename T, int D>
@@ -441,17 +472,10 @@ hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long g2 = (long long)p.B * p.Hkv * ((p.Nk + BT - 1) / BT);  // dK, dV: key tiles
   if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
-  if (p.causal) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3((unsigned)g2), dim3(NWB * 64), 0,
-                       stream, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3((unsigned)g1), dim3(NWB * 64), 0, stream,
-                       p);
-  } else {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3((unsigned)g2), dim3(NWB * 64), 0,
-                       stream, p);
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3((unsigned)g1), dim3(NWB * 64), 0,
-                       stream, p);
-  }
+  if (p.causal)
+    launch_grads<T, D, true>(p, g1, g2, stream);
+  else
+    launch_grads<T, D, false>(p, g1, g2, stream);
   return hipGetLastError();
 }
 
@@ -466,9 +490,11 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.dtype == DTYPE_BF16) {
+    if (p.d == 256) return launch_d<__bf16, 256>(p, stream);
     if (p.d == 128) return launch_d<__bf16, 128>(p, stream);
     if (p.d == 64) return launch_d<__bf16, 64>(p, stream);
   } else if (p.dtype == DTYPE_F16) {
+    if (p.d == 256) return launch_d<_Float16, 256>(p, stream);
     if (p.d == 128) return launch_d<_Float16, 128>(p, stream);
     if (p.d == 64) return launch_d<_Float16, 64>(p, stream);
   }

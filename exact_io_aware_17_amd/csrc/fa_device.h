@@ -24,13 +24,15 @@ constexpr float POS_INF = __builtin_huge_valf();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 
-// Forward K/V tiles (rows of D bf16). K rows are read whole (16 consecutive
-// rows at one chunk): chunk c of row `row` is stored at slot c ^ kswz(row).
-// V rows are read transposed (8 consecutive rows x 4 chunks at a time):
-// slot c ^ vswz(row).
+// Forward K/V tiles (rows of D 16-bit elements). K rows are read whole (16
+// consecutive rows at one chunk): chunk c of row `row` is stored at slot
+// c ^ kswz(row). V rows are read transposed (8 consecutive rows x 4 chunks at
+// a time): slot c ^ vswz(row). Rows of 256 or 512 bytes (D = 128, 256) all
+// start at LDS bank 0 and share one pattern.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  if constexpr (D == 128) {
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  if constexpr (D >= 128) {
     return row & 15;
   } else {
     return (row >> 1) & 7;
@@ -38,7 +40,7 @@ __device__ __forceinline__ int kswz(int row) {
 }
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return 4 * (row & 3);
   } else {
     return 4 * ((row >> 1) & 1);

@@ -89,8 +89,12 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 #define FA_FWD_WG_PER_CU 3
 #endif
 
+// Resident workgroups per CU the register budget is sized for: at D = 256 the
+// Q^T fragments and output accumulators alone take 192 registers per lane.
+constexpr int fwd_wg_per_cu(int D) { return D == 256 ? 1 : FA_FWD_WG_PER_CU; }
+
 template <typename T, int D, int BN, int STAGES, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, FA_FWD_WG_PER_CU) void fwd_kernel(FwdParams p, FwdPlan plan) {
+__global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParams p, FwdPlan plan) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
   constexpr int ROWB = D * 2;                 // bytes per K/V row
@@ -470,6 +474,7 @@ int occupancy() {
 
 template <typename T>
 int occupancy_of(int d, bool causal) {
+  if (d == 256) return causal ? occupancy<T, 256, true>() : occupancy<T, 256, false>();
   if (d == 128) return causal ? occupancy<T, 128, true>() : occupancy<T, 128, false>();
   if (d == 64) return causal ? occupancy<T, 64, true>() : occupancy<T, 64, false>();
   return 0;
@@ -479,9 +484,11 @@ int occupancy_of(int d, bool causal) {
 
 hipError_t launch_fwd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
   if (p.dtype == DTYPE_BF16) {
+    if (p.d == 256) return launch_d<__bf16, 256>(p, plan, stream);
     if (p.d == 128) return launch_d<__bf16, 128>(p, plan, stream);
     if (p.d == 64) return launch_d<__bf16, 64>(p, plan, stream);
   } else if (p.dtype == DTYPE_F16) {
+    if (p.d == 256) return launch_d<_Float16, 256>(p, plan, stream);
     if (p.d == 128) return launch_d<_Float16, 128>(p, plan, stream);
     if (p.d == 64) return launch_d<_Float16, 64>(p, plan, stream);
   }

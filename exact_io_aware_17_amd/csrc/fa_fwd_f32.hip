@@ -127,6 +127,7 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
+  if (p.d == 256) return launch_d<256>(p, stream);
   if (p.d == 128) return launch_d<128>(p, stream);
   if (p.d == 64) return launch_d<64>(p, stream);
   return hipErrorInvalidValue;

@@ -85,6 +85,7 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, lse=A + SZ + 64) == INV         # lse overlaps k
     assert _fwd(fn, d=96) == UNS
     assert _fwd(fn, d=32) == UNS
+    assert _fwd(fn, d=512) == UNS
     assert _fwd(fn, q=A + 2) == UNS                 # not 16-byte aligned
     assert _fwd(fn, kv=A + 5 * SZ + 2) == UNS       # kv_lens not 4-byte aligned
     assert _fwd(fn, B=1 << 16, H=1 << 16, N=1) == UNS  # row count beyond 32-bit
@@ -160,7 +161,8 @@ def test_bwd_argument_errors():
     p = list(base)
     p[7] = base[6]            # dk aliases dq
     assert call(p) == INV
-    assert call(d=256) == UNS
+    assert call(d=96) == UNS
+    assert call(d=512) == UNS
     p = list(base)
     p[9] = base[9] + 8        # workspace misaligned
     assert call(p) == UNS
