@@ -27,7 +27,7 @@ int check_common(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int 
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
       mask_kind != FA_MASK_CAUSAL_STRICT)
     return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   // Row indices (b*H + h)*Nq + i and (b*Hkv + h)*Nk + j are formed in 32-bit
   // arithmetic.
   if ((long long)B * H * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)

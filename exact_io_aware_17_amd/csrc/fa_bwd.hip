@@ -46,16 +46,31 @@ constexpr int BT = 32 * NWB;  // rows owned by a workgroup (queries in dq, keys 
 #define FA_BWD_DKDV128_OCC 2
 #endif
 
-// 16-byte chunk c of row `row` of a streamed tile is stored at c ^ tswz(row):
-// 16 consecutive rows read at one chunk, and 8 consecutive rows read 4 chunks
-// each by the transpose reads, both spread evenly over the LDS banks.
+// 16-byte chunk c of row `row` of a streamed tile is stored at slot
+// tslot(row, c): 16 consecutive rows read at one chunk, and 8 consecutive
+// rows read 4 chunks each by the transpose reads, both spread evenly over the
+// LDS banks. An XOR of the chunk index, except for the 12-chunk rows of
+// D = 96, which rotate by (row / 4) mod 4 instead.
 template <int D>
-__device__ __forceinline__ int tswz(int row) {
-  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+__device__ __forceinline__ int tslot(int row, int c) {
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dimension");
   if constexpr (D >= 128) {  // rows of 256 or 512 bytes: every row starts at bank 0
-    return 4 * (row & 3) + ((row >> 2) & 3);
+    return c ^ (4 * (row & 3) + ((row >> 2) & 3));
+  } else if constexpr (D == 64) {
+    return c ^ (((row >> 1) & 1) | (((row >> 2) & 1) << 2) | (((row >> 3) & 1) << 1));
+  } else if constexpr (D == 32) {
+    return c ^ ((row >> 2) & 3);
   } else {
-    return ((row >> 1) & 1) | (((row >> 2) & 1) << 2) | (((row >> 3) & 1) << 1);
+    return (c + ((row >> 2) & 3)) % 12;
+  }
+}
+// The chunk stored at slot s of row `row` (the inverse permutation).
+template <int D>
+__device__ __forceinline__ int tchunk(int row, int s) {
+  if constexpr (D == 96) {
+    return (s + 12 - ((row >> 2) & 3)) % 12;
+  } else {
+    return tslot<D>(row, s);
   }
 }
 
@@ -68,16 +83,21 @@ __device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
 __device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
 
 // ---- per row: D_i = sum_c dO_ic O_ic and lse_i * log2(e) ----
+template <int D>
+constexpr int prep_threads_per_row() {  // 8 elements per thread, a power of two threads
+  return D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   typedef Elem<T> E;
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  constexpr int TPR = prep_threads_per_row<D>();  // threads per row (the last ones idle at D = 96)
   constexpr int RPB = 256 / TPR;
   const long long rows = (long long)p.B * p.H * p.N;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = threadIdx.x % TPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && c < D / 8) {
     const u32x4 a = *(const u32x4*)((const T*)p.o + row * D + c * 8);
     const u32x4 g = *(const u32x4*)((const T*)p.dout + row * D + c * 8);
 #pragma unroll
@@ -95,25 +115,54 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// DMA of rows [r0, r0 + BS) of a row-major [N, D] 16-bit matrix into an LDS tile
-// (rows past N repeat row N-1; they are masked by the callers).
+// DMA of rows [r0, r0 + BS) of two row-major [N, D] 16-bit matrices X0, X1
+// into LDS tiles dst0, dst1 (rows past N repeat row N-1; they are masked by
+// the callers). Each DMA fills 1 KB (64 lanes x 16 bytes) of a tile. Where a
+// tile splits into whole rows per DMA and evenly over the waves (D = 64, 128,
+// 256), every wave loads its share of both tiles; otherwise (D = 32, 96) the
+// DMAs of both tiles form one list dealt round-robin over the waves, lane l
+// of DMA b covering slot 64 b + l of its tile in row-major order.
 template <int D>
-__device__ __forceinline__ void issue_tile(const void* __restrict__ Xv, int r0, int N, char* dst,
-                                           int wave, int lane) {
-  const unsigned short* __restrict__ X = (const unsigned short*)Xv;
+__device__ __forceinline__ void issue_tiles(const void* __restrict__ X0v,
+                                            const void* __restrict__ X1v, int r0, int N,
+                                            char* dst0, char* dst1, int wave, int lane) {
+  const unsigned short* __restrict__ X0 = (const unsigned short*)X0v;
+  const unsigned short* __restrict__ X1 = (const unsigned short*)X1v;
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int DMA_PER_TILE = BS * ROWB / 1024;
-  constexpr int DPW = DMA_PER_TILE / NWB;
-  constexpr int ROWS_PER_DMA = 1024 / ROWB;
-  static_assert(DMA_PER_TILE % NWB == 0, "tile DMAs split evenly over the waves");
+  static_assert((2 * DMA_PER_TILE) % NWB == 0, "the DMAs of two tiles split evenly over the waves");
+  if constexpr (1024 % ROWB == 0 && DMA_PER_TILE % NWB == 0) {
+    constexpr int DPW = DMA_PER_TILE / NWB;
+    constexpr int ROWS_PER_DMA = 1024 / ROWB;
 #pragma unroll
-  for (int e = 0; e < DPW; ++e) {
-    const int blk = wave * DPW + e;
-    const int row = blk * ROWS_PER_DMA + lane / CPR;
-    const int pch = lane % CPR;
-    const size_t src = (size_t)min(r0 + row, N - 1);
-    dma16(X + src * D + (pch ^ tswz<D>(row)) * 8, dst + blk * 1024);
+    for (int e = 0; e < DPW; ++e) {
+      const int blk = wave * DPW + e;
+      const int row = blk * ROWS_PER_DMA + lane / CPR;
+      const int pch = lane % CPR;
+      const size_t src = (size_t)min(r0 + row, N - 1);
+      dma16(X0 + src * D + tchunk<D>(row, pch) * 8, dst0 + blk * 1024);
+    }
+#pragma unroll
+    for (int e = 0; e < DPW; ++e) {
+      const int blk = wave * DPW + e;
+      const int row = blk * ROWS_PER_DMA + lane / CPR;
+      const int pch = lane % CPR;
+      const size_t src = (size_t)min(r0 + row, N - 1);
+      dma16(X1 + src * D + tchunk<D>(row, pch) * 8, dst1 + blk * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 2 * DMA_PER_TILE / NWB; ++m) {
+      const int e = wave + NWB * m;  // wave-uniform
+      const bool second = e >= DMA_PER_TILE;
+      const int blk = second ? e - DMA_PER_TILE : e;
+      const int g = 64 * blk + lane;
+      const int row = g / CPR;
+      const size_t src = (size_t)min(r0 + row, N - 1);
+      dma16((second ? X1 : X0) + src * D + tchunk<D>(row, g % CPR) * 8,
+            (second ? dst1 : dst0) + blk * 1024);
+    }
   }
 }
 
@@ -130,7 +179,7 @@ struct TileOffsets {
     constexpr int ROWB = D * 2;
     const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) roff[c] = n * ROWB + (((2 * c + h) ^ tswz<D>(n)) * 16);
+    for (int c = 0; c < D / 16; ++c) roff[c] = n * ROWB + tslot<D>(n, 2 * c + h) * 16;
     const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int vrow = 4 * h + ((lane & 15) >> 2);
 #pragma unroll
@@ -139,7 +188,7 @@ struct TileOffsets {
       for (int r = 0; r < 2; ++r) {
         const int row = 8 * r + vrow;
         const int col = dt * 32 + vcol;
-        toff[dt][r] = row * ROWB + (((col >> 3) ^ tswz<D>(row)) * 16) + (col & 7) * 2;
+        toff[dt][r] = row * ROWB + tslot<D>(row, col >> 3) * 16 + (col & 7) * 2;
       }
   }
 };
@@ -224,8 +273,7 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
 
   auto issue = [&](int j) {
     if (j >= nblk) return;
-    issue_tile<D>(K, j * BS, Nk, kbuf[j & 1], wave, lane);
-    issue_tile<D>(V, j * BS, Nk, vbuf[j & 1], wave, lane);
+    issue_tiles<D>(K, V, j * BS, Nk, kbuf[j & 1], vbuf[j & 1], wave, lane);
   };
   issue(0);
   for (int j = 0; j < nblk; ++j) {
@@ -346,8 +394,8 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     if (u >= nsteps) return;
     const int g = u / nq, i = qstart + u % nq;
     const size_t qh = qhead0 + g;
-    issue_tile<D>((const T*)p.q + qh * N * D, i * BS, N, qbuf[u & 1], wave, lane);
-    issue_tile<D>((const T*)p.dout + qh * N * D, i * BS, N, obuf[u & 1], wave, lane);
+    issue_tiles<D>((const T*)p.q + qh * N * D, (const T*)p.dout + qh * N * D, i * BS, N,
+                   qbuf[u & 1], obuf[u & 1], wave, lane);
     if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
       const int qi = min(i * BS + (lane & 31), N - 1);
       const float* src = ((lane < 32) ? p.lse2 : p.delta) + qh * N + qi;
@@ -466,7 +514,7 @@ void launch_grads(const BwdParams& p, long long g1, long long g2, hipStream_t st
 template <typename T, int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
-  const long long rpb = 256 / (D / 8);
+  const long long rpb = 256 / prep_threads_per_row<D>();
   const long long g0 = (rows + rpb - 1) / rpb;
   const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);     // dQ: query tiles
   const long long g2 = (long long)p.B * p.Hkv * ((p.Nk + BT - 1) / BT);  // dK, dV: key tiles
@@ -489,15 +537,13 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  if (p.dtype == DTYPE_BF16) {
-    if (p.d == 256) return launch_d<__bf16, 256>(p, stream);
-    if (p.d == 128) return launch_d<__bf16, 128>(p, stream);
-    if (p.d == 64) return launch_d<__bf16, 64>(p, stream);
-  } else if (p.dtype == DTYPE_F16) {
-    if (p.d == 256) return launch_d<_Float16, 256>(p, stream);
-    if (p.d == 128) return launch_d<_Float16, 128>(p, stream);
-    if (p.d == 64) return launch_d<_Float16, 64>(p, stream);
+#define FA_LAUNCH(DD)                                                     \
+  if (p.d == DD) {                                                        \
+    if (p.dtype == DTYPE_BF16) return launch_d<__bf16, DD>(p, stream);   \
+    if (p.dtype == DTYPE_F16) return launch_d<_Float16, DD>(p, stream);  \
   }
+  FA_LAUNCH(32) FA_LAUNCH(64) FA_LAUNCH(96) FA_LAUNCH(128) FA_LAUNCH(256)
+#undef FA_LAUNCH
   return hipErrorInvalidValue;
 }
 

@@ -24,27 +24,53 @@ constexpr float POS_INF = __builtin_huge_valf();
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
 
-// Forward K/V tiles (rows of D 16-bit elements). K rows are read whole (16
-// consecutive rows at one chunk): chunk c of row `row` is stored at slot
-// c ^ kswz(row). V rows are read transposed (8 consecutive rows x 4 chunks at
-// a time): slot c ^ vswz(row). Rows of 256 or 512 bytes (D = 128, 256) all
-// start at LDS bank 0 and share one pattern.
+// Forward K/V tiles (rows of D 16-bit elements, D * 2 / 16 chunks of 16
+// bytes). Chunk c of row `row` is stored at slot kslot(row, c) (K) or
+// vslot(row, c) (V) of that row, a per-row permutation chosen so that the
+// operand reads spread over all 64 LDS banks (4-byte banks; 16 lanes of a
+// 16-byte read, or 32 lanes of an 8-byte read, per pass):
+//  * K rows are read whole: 16 consecutive rows at one chunk;
+//  * V rows are read transposed: 4 consecutive rows x 4 chunks per half-wave.
+// Rows of 256 or 512 bytes (D = 128, 256) all start at bank 0 and share one
+// pattern; 64-byte rows (D = 32) cycle through the banks every 4 rows, so
+// K slots are XORed with row / 4; 192-byte rows (D = 96) have 12 chunks, so
+// K slots are rotated by (row / 4) mod 4 instead (an XOR would leave the
+// row). The V reads of D = 32 and 96 are conflict-free unpermuted.
 template <int D>
-__device__ __forceinline__ int kswz(int row) {
-  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+__device__ __forceinline__ int kslot(int row, int c) {
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dimension");
   if constexpr (D >= 128) {
-    return row & 15;
+    return c ^ (row & 15);
+  } else if constexpr (D == 64) {
+    return c ^ ((row >> 1) & 7);
+  } else if constexpr (D == 32) {
+    return c ^ ((row >> 2) & 3);
   } else {
-    return (row >> 1) & 7;
+    return (c + ((row >> 2) & 3)) % 12;
+  }
+}
+// The chunk stored at slot s of K row `row` (the inverse permutation).
+template <int D>
+__device__ __forceinline__ int kchunk(int row, int s) {
+  if constexpr (D == 96) {
+    return (s + 12 - ((row >> 2) & 3)) % 12;
+  } else {
+    return kslot<D>(row, s);  // an XOR is its own inverse
   }
 }
 template <int D>
-__device__ __forceinline__ int vswz(int row) {
+__device__ __forceinline__ int vslot(int row, int c) {
   if constexpr (D >= 128) {
-    return 4 * (row & 3);
+    return c ^ (4 * (row & 3));
+  } else if constexpr (D == 64) {
+    return c ^ (4 * ((row >> 1) & 1));
   } else {
-    return 4 * ((row >> 1) & 1);
+    return c;
   }
+}
+template <int D>
+__device__ __forceinline__ int vchunk(int row, int s) {
+  return vslot<D>(row, s);  // an XOR or the identity: its own inverse
 }
 
 // Position of index x inside its 16-group of a transposed tile: bits 2 and 3

@@ -93,6 +93,9 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 // Q^T fragments and output accumulators alone take 192 registers per lane.
 constexpr int fwd_wg_per_cu(int D) { return D == 256 ? 1 : FA_FWD_WG_PER_CU; }
 
+// Head dimensions with kernel instances.
+#define FA_FOR_EACH_D(X) X(32) X(64) X(96) X(128) X(256)
+
 template <typename T, int D, int BN, int STAGES, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParams p, FwdPlan plan) {
   typedef Elem<T> E;
@@ -101,13 +104,19 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
   constexpr int TILE = BN * ROWB;             // bytes per K or V tile
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
   constexpr int DMA_PER_TILE = TILE / 1024;   // 1 KB (64 lanes x 16 B) per DMA instruction
-  constexpr int DPW = DMA_PER_TILE / NW;      // DMA instructions per wave per tile
-  constexpr int ROWS_PER_DMA = 1024 / ROWB;
+  // Whole rows per DMA and an equal share of the K and of the V DMAs per wave
+  // (D = 64, 128, 256); otherwise (D = 32, 96) the K and V DMAs of a block
+  // form one list dealt round-robin over the waves, each DMA covering 64
+  // consecutive 16-byte slots of its tile in row-major order.
+  constexpr bool ROWWISE = (1024 % ROWB == 0) && (DMA_PER_TILE % NW == 0);
+  constexpr int DPW = ROWWISE ? DMA_PER_TILE / NW : 1;  // per wave per tile (row-wise)
+  constexpr int ROWS_PER_DMA = ROWWISE ? 1024 / ROWB : 1;
+  constexpr int MPW = 2 * DMA_PER_TILE / NW;  // per wave per block (dealt)
   constexpr int DC = D / 16;                  // 16-wide d chunks (S contraction)
   constexpr int DT = D / 32;                  // 32-row d tiles of O^T
   constexpr int KT = BN / 32;                 // 32-key MFMA tiles per block
   constexpr int KC = BN / 16;                 // 16-key contraction chunks per block
-  static_assert(DMA_PER_TILE % NW == 0, "DMA blocks must split evenly over the waves");
+  static_assert((2 * DMA_PER_TILE) % NW == 0, "the DMAs of a block split evenly over the waves");
   static_assert(BN == 32 || BN == 64, "block of 32 or 64 keys");
   static_assert(STAGES == 2, "double-buffered K/V stream");
 
@@ -182,12 +191,28 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
   // block's DMA then needs only a scalar base. A block that runs past row
   // N-1 (the ragged end) takes the clamped path.
   int gk[DPW], gv[DPW];
+  if constexpr (ROWWISE) {
 #pragma unroll
-  for (int i = 0; i < DPW; ++i) {
-    const int row = (wave * DPW + i) * ROWS_PER_DMA + lane / CPR;
-    const int pch = lane % CPR;
-    gk[i] = row * ROWB + (pch ^ kswz<D>(row)) * 16;
-    gv[i] = row * ROWB + (pch ^ vswz<D>(row)) * 16;
+    for (int i = 0; i < DPW; ++i) {
+      const int row = (wave * DPW + i) * ROWS_PER_DMA + lane / CPR;
+      const int pch = lane % CPR;
+      gk[i] = row * ROWB + kchunk<D>(row, pch) * 16;
+      gv[i] = row * ROWB + vchunk<D>(row, pch) * 16;
+    }
+  }
+  // Dealt DMAs: the m-th of this wave is entry wave + NW*m of the block's list
+  // (K tile DMAs first, then V); lane l covers slot 64*blk + l of its tile.
+  int grow[MPW], gch[MPW], goff[MPW];
+  if constexpr (!ROWWISE) {
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const int e = wave + NW * m;
+      const bool isv = e >= DMA_PER_TILE;
+      const int g = 64 * (isv ? e - DMA_PER_TILE : e) + lane;
+      grow[m] = g / CPR;
+      gch[m] = isv ? vchunk<D>(grow[m], g % CPR) : kchunk<D>(grow[m], g % CPR);
+      goff[m] = grow[m] * ROWB + gch[m] * 16;
+    }
   }
   auto issue_block = [&](int j, auto stage) {
     constexpr int SD = decltype(stage)::value;
@@ -195,6 +220,24 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
     const int key0 = j * BN;
     char* ks = kbuf[SD];
     char* vs = vbuf[SD];
+    if constexpr (!ROWWISE) {
+      const char* kb = (const char*)(K + (size_t)key0 * D);
+      const char* vb = (const char*)(V + (size_t)key0 * D);
+      const bool full = key0 + BN <= Nk;
+#pragma unroll
+      for (int m = 0; m < MPW; ++m) {
+        const int e = wave + NW * m;  // wave-uniform
+        const bool isv = e >= DMA_PER_TILE;
+        char* dst = (isv ? vs : ks) + (isv ? e - DMA_PER_TILE : e) * 1024;
+        if (full) {
+          dma16((isv ? vb : kb) + goff[m], dst);
+        } else {
+          const size_t key = (size_t)min(key0 + grow[m], Nk - 1);
+          dma16((isv ? V : K) + key * D + gch[m] * 8, dst);
+        }
+      }
+      return;
+    }
     if (key0 + BN <= Nk) {
       const char* kb = (const char*)(K + (size_t)key0 * D);
       const char* vb = (const char*)(V + (size_t)key0 * D);
@@ -211,8 +254,8 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
         const int row = blk * ROWS_PER_DMA + lane / CPR;
         const int pch = lane % CPR;
         const size_t key = (size_t)min(key0 + row, Nk - 1);
-        dma16(K + key * D + (pch ^ kswz<D>(row)) * 8, ks + blk * 1024);
-        dma16(V + key * D + (pch ^ vswz<D>(row)) * 8, vs + blk * 1024);
+        dma16(K + key * D + kchunk<D>(row, pch) * 8, ks + blk * 1024);
+        dma16(V + key * D + vchunk<D>(row, pch) * 8, vs + blk * 1024);
       }
     }
   };
@@ -220,17 +263,17 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
   // Per-lane LDS offsets of the operand reads (the block-independent parts).
   int koff[DC];  // K row n (+32 per key tile), logical chunk 2c + h
 #pragma unroll
-  for (int c = 0; c < DC; ++c) koff[c] = n * ROWB + (((2 * c + h) ^ kswz<D>(n)) * 16);
+  for (int c = 0; c < DC; ++c) koff[c] = n * ROWB + kslot<D>(n, 2 * c + h) * 16;
   // V^T transpose reads: row 16*kc + 8r + 4h + (lane%16)/4, column
-  // dt*32 + 16*((lane/16)%2) + 4*(lane%4) (four elements = 8 bytes). The swizzle
-  // depends only on the row's low bits, which 16*kc + 8r leaves unchanged.
+  // dt*32 + 16*((lane/16)%2) + 4*(lane%4) (four elements = 8 bytes). The slot
+  // permutation depends only on row % 8, which 16*kc + 8r leaves unchanged.
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vrow = 4 * h + ((lane & 15) >> 2);
   int voff[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const int col = dt * 32 + vcol;
-    voff[dt] = vrow * ROWB + (((col >> 3) ^ vswz<D>(vrow)) * 16) + (col & 7) * 2;
+    voff[dt] = vrow * ROWB + vslot<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
   }
 
   f32x16 acc[DT];
@@ -474,24 +517,23 @@ int occupancy() {
 
 template <typename T>
 int occupancy_of(int d, bool causal) {
-  if (d == 256) return causal ? occupancy<T, 256, true>() : occupancy<T, 256, false>();
-  if (d == 128) return causal ? occupancy<T, 128, true>() : occupancy<T, 128, false>();
-  if (d == 64) return causal ? occupancy<T, 64, true>() : occupancy<T, 64, false>();
+#define FA_OCC(DD) \
+  if (d == DD) return causal ? occupancy<T, DD, true>() : occupancy<T, DD, false>();
+  FA_FOR_EACH_D(FA_OCC)
+#undef FA_OCC
   return 0;
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-  if (p.dtype == DTYPE_BF16) {
-    if (p.d == 256) return launch_d<__bf16, 256>(p, plan, stream);
-    if (p.d == 128) return launch_d<__bf16, 128>(p, plan, stream);
-    if (p.d == 64) return launch_d<__bf16, 64>(p, plan, stream);
-  } else if (p.dtype == DTYPE_F16) {
-    if (p.d == 256) return launch_d<_Float16, 256>(p, plan, stream);
-    if (p.d == 128) return launch_d<_Float16, 128>(p, plan, stream);
-    if (p.d == 64) return launch_d<_Float16, 64>(p, plan, stream);
+#define FA_LAUNCH(DD)                                            \
+  if (p.d == DD) {                                               \
+    if (p.dtype == DTYPE_BF16) return launch_d<__bf16, DD>(p, plan, stream);   \
+    if (p.dtype == DTYPE_F16) return launch_d<_Float16, DD>(p, plan, stream);  \
   }
+  FA_FOR_EACH_D(FA_LAUNCH)
+#undef FA_LAUNCH
   return hipErrorInvalidValue;
 }
 

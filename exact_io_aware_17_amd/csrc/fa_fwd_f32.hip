@@ -129,7 +129,9 @@ hipError_t launch_d(const FwdParams& p, hipStream_t stream) {
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
   if (p.d == 256) return launch_d<256>(p, stream);
   if (p.d == 128) return launch_d<128>(p, stream);
+  if (p.d == 96) return launch_d<96>(p, stream);
   if (p.d == 64) return launch_d<64>(p, stream);
+  if (p.d == 32) return launch_d<32>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -47,7 +47,7 @@
  *   FA_ERR_INVALID_ARG  null tensor pointer, B/H/Hkv/Nq/Nk <= 0, H not a
  *                       multiple of Hkv, scale not finite or not > 0,
  *                       unknown mask_kind, an output overlapping an input;
- *   FA_ERR_UNSUPPORTED  d not supported (64, 128 and 256 are), a tensor pointer
+ *   FA_ERR_UNSUPPORTED  d not supported (32, 64, 96, 128 and 256 are), a tensor pointer
  *                       not 16-byte aligned, sizes whose element count does
  *                       not fit the kernels' 32-bit row indices;
  *   FA_ERR_HIP          the launch itself failed (hipGetLastError).

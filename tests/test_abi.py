@@ -83,8 +83,8 @@ def test_fwd_argument_errors(fn):
     assert _fwd(fn, mask=-1) == INV
     assert _fwd(fn, o=A + 8) == INV                 # output overlaps q
     assert _fwd(fn, lse=A + SZ + 64) == INV         # lse overlaps k
-    assert _fwd(fn, d=96) == UNS
-    assert _fwd(fn, d=32) == UNS
+    assert _fwd(fn, d=80) == UNS
+    assert _fwd(fn, d=16) == UNS
     assert _fwd(fn, d=512) == UNS
     assert _fwd(fn, q=A + 2) == UNS                 # not 16-byte aligned
     assert _fwd(fn, kv=A + 5 * SZ + 2) == UNS       # kv_lens not 4-byte aligned
@@ -161,7 +161,7 @@ def test_bwd_argument_errors():
     p = list(base)
     p[7] = base[6]            # dk aliases dq
     assert call(p) == INV
-    assert call(d=96) == UNS
+    assert call(d=48) == UNS
     assert call(d=512) == UNS
     p = list(base)
     p[9] = base[9] + 8        # workspace misaligned
@@ -184,7 +184,7 @@ def test_bwd_ex_argument_errors():
     assert call(Hkv=0) == INV
     assert call(Nk=0) == INV
     assert call(Nq=0) == INV
-    assert call(d=32) == UNS
+    assert call(d=160) == UNS
     # k is [1, 2, 32, 64] bf16 = 8 KiB: dk over its last 16 bytes, and dk just
     # past its end, which overlaps it once k has 33 rows.
     p = list(base)
