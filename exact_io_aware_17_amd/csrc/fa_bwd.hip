@@ -29,6 +29,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -225,8 +227,13 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
   constexpr int DC = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char kbuf[2][TB];  // K block, row-major
-  __shared__ __attribute__((aligned(1024))) char vbuf[2][TB];  // V block, row-major
+  // K and V blocks, row-major, one LDS object per stage (so that the
+  // compiler sees that the next block's DMA cannot alias this block's reads
+  // and does not wait for it before them).
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -271,19 +278,22 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
 #pragma unroll
   for (int t = 0; t < DT; ++t) zero(acc[t]);
 
-  auto issue = [&](int j) {
+  // Block j lives in stage j % 2; the loop is unrolled by the two stages so
+  // that every buffer is a compile-time choice.
+  auto issue = [&](int j, auto stage) {
+    constexpr int SD = decltype(stage)::value;
     if (j >= nblk) return;
-    issue_tiles<D>(K, V, j * BS, Nk, kbuf[j & 1], vbuf[j & 1], wave, lane);
+    issue_tiles<D>(K, V, j * BS, Nk, SD == 0 ? kbuf0 : kbuf1, SD == 0 ? vbuf0 : vbuf1, wave, lane);
   };
-  issue(0);
-  for (int j = 0; j < nblk; ++j) {
+  auto step = [&](int j, auto stage) {
+    constexpr int ST = decltype(stage)::value;
     wait_vmem();
     __syncthreads();
-    issue(j + 1);
+    issue(j + 1, std::integral_constant<int, 1 - ST>());
     const int key0 = j * BS;
-    if (CAUSAL && key0 > qa + 31 + shift) continue;  // wholly in this wave's future
-    const char* ks = kbuf[j & 1];
-    const char* vs = vbuf[j & 1];
+    if (CAUSAL && key0 > qa + 31 + shift) return;  // wholly in this wave's future
+    const char* ks = ST == 0 ? kbuf0 : kbuf1;
+    const char* vs = ST == 0 ? vbuf0 : vbuf1;
 
     __builtin_amdgcn_s_setprio(1);
     f32x16 s, dp;
@@ -323,6 +333,11 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) acc[dt] = E::mfma(tr_operand<x8, D>(ks, off, dt, kc), df[kc], acc[dt]);
     __builtin_amdgcn_s_setprio(0);
+  };
+  issue(0, std::integral_constant<int, 0>());
+  for (int j = 0; j < nblk; j += 2) {
+    step(j, std::integral_constant<int, 0>());
+    if (j + 1 < nblk) step(j + 1, std::integral_constant<int, 1>());
   }
   wait_vmem();
 
@@ -343,9 +358,21 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   typedef typename E::x8 x8;
   constexpr int TB = BS * D * 2;
   constexpr int DC = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char qbuf[2][TB];  // Q block, row-major
-  __shared__ __attribute__((aligned(1024))) char obuf[2][TB];  // dO block, row-major
-  __shared__ __attribute__((aligned(16))) float stat[2][64];   // lse*log2(e), then D
+  // Q and dO blocks (row-major) and their lse*log2(e), then D values: one
+  // LDS object per stage, as in the dQ kernel.
+  __shared__ __attribute__((aligned(1024))) char qbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) char obuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char obuf1[TB];
+  __shared__ __attribute__((aligned(16))) float stat0[64];
+  __shared__ __attribute__((aligned(16))) float stat1[64];
+  // At D = 128 the K operand fragments of this workgroup's keys wait in LDS
+  // (32 KB; each lane reads back its own 16-byte slots, free of bank
+  // conflicts) rather than in 32 registers: with them in registers the
+  // kernel exceeds the 256 registers of two waves per SIMD, and the spill
+  // reload waits for every outstanding load, the next block's DMA included.
+  constexpr bool KF_LDS = (D == 128) && (OUT == (DKDV_V | DKDV_K));
+  __shared__ __attribute__((aligned(1024))) char kfl[KF_LDS ? NWB * DC * 1024 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -367,10 +394,14 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   const int kw0 = kb0 + wave * 32;
   const int key = kw0 + n;
   const int key_c = min(key, Nk - 1);
-  x8 kf[DC], vf[(OUT & DKDV_K) ? DC : 1];
+  x8 kf[KF_LDS ? 1 : DC], vf[(OUT & DKDV_K) ? DC : 1];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    kf[c] = *(const x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
+    const x8 kc = *(const x8*)(K + (size_t)key_c * D + 16 * c + 8 * h);
+    if constexpr (KF_LDS)
+      *(x8*)(kfl + (wave * DC + c) * 1024 + lane * 16) = kc;  // read back by this lane only
+    else
+      kf[c] = kc;
     if constexpr ((OUT & DKDV_K) != 0) vf[c] = *(const x8*)(V + (size_t)key_c * D + 16 * c + 8 * h);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -390,29 +421,31 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   const int qstart = CAUSAL ? min(max(kb0 - shift, 0) / BS, nqb) : 0;
   const int nq = nqb - qstart;
   const int nsteps = (kb0 < kvlen) ? G * nq : 0;  // every key of the tile hidden: nothing to do
-  auto issue = [&](int u) {
+  auto issue = [&](int u, auto stage) {
+    constexpr int SD = decltype(stage)::value;
     if (u >= nsteps) return;
     const int g = u / nq, i = qstart + u % nq;
     const size_t qh = qhead0 + g;
     issue_tiles<D>((const T*)p.q + qh * N * D, (const T*)p.dout + qh * N * D, i * BS, N,
-                   qbuf[u & 1], obuf[u & 1], wave, lane);
+                   SD == 0 ? qbuf0 : qbuf1, SD == 0 ? obuf0 : obuf1, wave, lane);
     if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
       const int qi = min(i * BS + (lane & 31), N - 1);
       const float* src = ((lane < 32) ? p.lse2 : p.delta) + qh * N + qi;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)stat[u & 1], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(SD == 0 ? stat0 : stat1), 4, 0, 0);
     }
   };
-  issue(0);
-  for (int u = 0; u < nsteps; ++u) {
+  // Step u uses stage u % 2; unrolled by the two stages as in the dQ kernel.
+  auto step = [&](int u, auto stage) {
+    constexpr int ST = decltype(stage)::value;
     wait_vmem();
     __syncthreads();
-    issue(u + 1);
+    issue(u + 1, std::integral_constant<int, 1 - ST>());
     const int qb0 = (qstart + u % nq) * BS;
-    if (kw0 >= kvlen) continue;                         // all of this wave's keys are hidden
-    if (CAUSAL && kw0 > qb0 + BS - 1 + shift) continue;  // every query of the block precedes them
-    const char* qs = qbuf[u & 1];
-    const char* os = obuf[u & 1];
-    const float* st = stat[u & 1];
+    if (kw0 >= kvlen) return;                         // all of this wave's keys are hidden
+    if (CAUSAL && kw0 > qb0 + BS - 1 + shift) return;  // every query of the block precedes them
+    const char* qs = ST == 0 ? qbuf0 : qbuf1;
+    const char* os = ST == 0 ? obuf0 : obuf1;
+    const float* st = ST == 0 ? stat0 : stat1;
 
     // Phases in order, each value dead as soon as it is consumed: S, P, dV^T
     // (needs P), dP, dS (needs P and dP), dK^T.
@@ -420,7 +453,14 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     f32x16 s;
     zero(s);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) s = E::mfma(*(const x8*)(qs + off.roff[c]), kf[c], s);
+    for (int c = 0; c < DC; ++c) {
+      x8 kc;
+      if constexpr (KF_LDS)
+        kc = *(const x8*)(kfl + (wave * DC + c) * 1024 + lane * 16);
+      else
+        kc = kf[c];
+      s = E::mfma(*(const x8*)(qs + off.roff[c]), kc, s);
+    }
     __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0 + shift);
 #pragma unroll
@@ -456,7 +496,7 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     }
     if constexpr ((OUT & DKDV_K) == 0) {
       __builtin_amdgcn_s_setprio(0);
-      continue;
+      return;
     }
     f32x16 dp;
     zero(dp);
@@ -485,6 +525,11 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) dka[dt] = E::mfma(tr_operand<x8, D>(qs, off, dt, qc), df[qc], dka[dt]);
     __builtin_amdgcn_s_setprio(0);
+  };
+  issue(0, std::integral_constant<int, 0>());
+  for (int u = 0; u < nsteps; u += 2) {
+    step(u, std::integral_constant<int, 0>());
+    if (u + 1 < nsteps) step(u + 1, std::integral_constant<int, 1>());
   }
   wait_vmem();
 

@@ -25,9 +25,9 @@
 //    give each lane four keys of one d column.
 //  * K and V tiles go from HBM to LDS with direct 16-byte loads (no register
 //    staging) into two buffers: block j+1 is in flight while block j is
-//    used. 16-byte chunks are XOR-swizzled per row so the operand reads hit
-//    every LDS bank evenly. The loop is unrolled by two so that each
-//    buffer's LDS offsets are immediates, and each lane's source offsets
+//    used. The 16-byte chunks of a row are permuted per row so the operand
+//    reads hit every LDS bank evenly. The loop is unrolled by two so that
+//    each buffer's LDS offsets are immediates, and each lane's source offsets
 //    within a block are computed once.
 //  * Registers are kept low enough for several waves per SIMD: their
 //    interleaving hides LDS and MFMA latency and overlaps one wave's softmax
@@ -120,8 +120,14 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
   static_assert(BN == 32 || BN == 64, "block of 32 or 64 keys");
   static_assert(STAGES == 2, "double-buffered K/V stream");
 
-  __shared__ __attribute__((aligned(1024))) char kbuf[STAGES][TILE];
-  __shared__ __attribute__((aligned(1024))) char vbuf[STAGES][TILE];
+  // One LDS object per stage and operand: the compiler then knows that the
+  // DMA into one stage cannot alias the reads of the other, and the block's
+  // first LDS read need not wait for the next block's DMA (with one array per
+  // operand it waits for every outstanding DMA, serialising the prefetch).
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TILE];
   __shared__ int s_arrival;
 
   const int tid = threadIdx.x;
@@ -218,8 +224,8 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
     constexpr int SD = decltype(stage)::value;
     if (j >= jend) return;
     const int key0 = j * BN;
-    char* ks = kbuf[SD];
-    char* vs = vbuf[SD];
+    char* ks = SD == 0 ? kbuf0 : kbuf1;
+    char* vs = SD == 0 ? vbuf0 : vbuf1;
     if constexpr (!ROWWISE) {
       const char* kb = (const char*)(K + (size_t)key0 * D);
       const char* vb = (const char*)(V + (size_t)key0 * D);
@@ -299,8 +305,8 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
     const int key0 = j * BN;
     // Skip blocks wholly in this wave's future (all its rows would be masked).
     if (CAUSAL && key0 > qa + 31 + shift) return;
-    const char* ks = kbuf[ST];
-    const char* vs = vbuf[ST];
+    const char* ks = ST == 0 ? kbuf0 : kbuf1;
+    const char* vs = ST == 0 ? vbuf0 : vbuf1;
 
     // ---- S^T = K Q^T for BN keys x 32 queries ----
     // Waves in a matrix phase get issue priority over waves in their softmax,
