@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -44,7 +44,7 @@ SIGNATURES = {
                     _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
-    "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
 }
@@ -193,13 +193,14 @@ def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def schedule(N: int, BH: int, causal, cus: int, occ: int, Nk: Optional[int] = None):
+def schedule(N: int, BH: int, causal, cus: int, occ: int, Nk: Optional[int] = None,
+             d: int = 128):
     """fa_fwd_schedule: (items, nslots) of fa_fwd_ex's work plan (host only);
-    N query rows, Nk keys (default N)."""
+    N query rows, Nk keys (default N), head dimension d."""
     lib = load()
     buf = (ctypes.c_uint32 * 4096)()
     ns = ctypes.c_int(0)
-    n = lib.fa_fwd_schedule(N, N if Nk is None else Nk, BH, mask_kind(causal), cus, occ, buf,
+    n = lib.fa_fwd_schedule(N, N if Nk is None else Nk, BH, d, mask_kind(causal), cus, occ, buf,
                             4096, ctypes.byref(ns))
     if n < 0:
         raise FaError("fa_fwd_schedule", n, status_string(n))

@@ -114,7 +114,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     const int BH = B * H;
     int cus = 0, occ = 0;
     fa::fwd_occupancy(d, p.causal != 0, p.dtype, &cus, &occ);
-    const fa::FwdPlan& cand = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, cus, occ);
+    const fa::FwdPlan& cand =
+        fa::fwd_plan(Nq, Nk, BH, p.causal != 0, fa::fwd_block_keys(d), cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, Nq, d);
     if (cand.nitems > 0 && workspace_bytes >= w.total) {
       plan = &cand;
@@ -219,7 +220,7 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
   const bool causal = (mask_kind != FA_MASK_NONE);
   int cus = 0, occ = 0;
   fa::fwd_occupancy(d, causal, dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16, &cus, &occ);
-  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, cus, occ);
+  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, fa::fwd_block_keys(d), cus, occ);
   return fa::fwd_workspace_layout(plan, B * H, Nq, d).total;
 }
 
@@ -236,15 +237,16 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                     nullptr, 0, stream);
 }
 
-int fa_fwd_schedule(int Nq, int Nk, int BH, int mask_kind, int cus, int occ, uint32_t* items,
-                    int max_items, int* nslots) {
-  if (Nq <= 0 || Nk <= 0 || BH <= 0 || cus < 0 || occ < 0 || max_items < 0 ||
+int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int occ,
+                    uint32_t* items, int max_items, int* nslots) {
+  if (Nq <= 0 || Nk <= 0 || BH <= 0 || d <= 0 || cus < 0 || occ < 0 || max_items < 0 ||
       (max_items > 0 && !items))
     return FA_ERR_INVALID_ARG;
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
       mask_kind != FA_MASK_CAUSAL_STRICT)
     return FA_ERR_INVALID_ARG;
-  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, BH, mask_kind != FA_MASK_NONE, cus, occ);
+  const fa::FwdPlan& plan =
+      fa::fwd_plan(Nq, Nk, BH, mask_kind != FA_MASK_NONE, fa::fwd_block_keys(d), cus, occ);
   for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
   if (nslots) *nslots = plan.nslots;
   return plan.nitems;

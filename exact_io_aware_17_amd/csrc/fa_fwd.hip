@@ -76,9 +76,6 @@ static_assert(BM == FWD_BM, "workgroup tile matches the host planner");
 constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
 constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 
-#ifndef FA_FWD_BN
-#define FA_FWD_BN FWD_BN
-#endif
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 2
 #endif
@@ -496,8 +493,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
 
 template <typename T, int D>
 hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-  constexpr int BN = FA_FWD_BN, ST = FA_FWD_STAGES;
-  static_assert(BN == FWD_BN, "the host planner counts blocks of FWD_BN keys");
+  constexpr int BN = fwd_block_keys(D), ST = FA_FWD_STAGES;  // the planner counts these blocks
   const long long ntiles = (p.N + BM - 1) / BM;
   const long long items = plan.nitems > 0 ? plan.nitems : ntiles;
   const long long grid = (long long)p.B * p.H * items;
@@ -515,7 +511,7 @@ template <typename T, int D, bool CAUSAL>
 int occupancy() {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, FA_FWD_BN, FA_FWD_STAGES, CAUSAL>),
+          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, fwd_block_keys(D), FA_FWD_STAGES, CAUSAL>),
           NW * 64, 0) != hipSuccess)
     return 0;
   return per;

@@ -35,7 +35,10 @@ struct FwdParams {
 
 // Forward tiling shared by the kernel and the host planner.
 constexpr int FWD_BM = 128;                 // query rows per workgroup
-constexpr int FWD_BN = 32;                  // keys per streamed block
+// Keys per streamed block: 64 for head dimensions up to 64 (each block's
+// fixed costs, its barrier and its softmax bookkeeping, then meet as much
+// matrix work as a 32-key block at d = 128), 32 above.
+constexpr int fwd_block_keys(int d) { return d <= 64 ? 64 : 32; }
 constexpr int FWD_ML_FLOATS = 4 * 2 * FWD_BM;  // {m, l, l_bf, 0} for each of 2*BM lanes
 constexpr int FWD_PLAN_MAX = 512;
 // Arrival counters occupy a fixed region at the start of every forward
@@ -57,9 +60,10 @@ struct FwdPlan {
 // Balancing plan for N query rows against Nk keys, BH query heads, `cus`
 // compute units and `occ` resident workgroups per compute unit (cached; the
 // reference stays valid).
-const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int cus, int occ);
+// Blocks are of bn keys (fwd_block_keys(d)).
+const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ);
 // Nominal key blocks of query tile t (causal: bottom-right aligned).
-int fwd_tile_blocks(int N, int Nk, int t, bool causal);
+int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn);
 // Workspace layout for a plan: byte offsets of counters, part_ml, part_o and the total.
 struct FwdWorkspace {
   size_t counters, part_ml, part_o, total;

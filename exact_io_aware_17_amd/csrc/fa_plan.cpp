@@ -30,11 +30,11 @@
 
 namespace fa {
 
-int fwd_tile_blocks(int N, int Nk, int t, bool causal) {
+int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn) {
   long long kend = Nk;
   if (causal) kend = std::min<long long>(Nk, (long long)(t + 1) * FWD_BM + (long long)Nk - N);
   if (kend <= 0) return 0;
-  return (int)((kend + FWD_BN - 1) / FWD_BN);
+  return (int)((kend + bn - 1) / bn);
 }
 
 namespace {
@@ -123,11 +123,11 @@ double simulate(const std::vector<Item>& items, int BH, int cus, int occ) {
 
 // Items for split threshold T (blocks): tiles above T are cut into
 // min(4, ceil(nb / T)) parts. T <= 0 means no split.
-std::vector<Item> make_items(int N, int Nk, bool causal, int T) {
+std::vector<Item> make_items(int N, int Nk, bool causal, int bn, int T) {
   const int ntiles = (N + FWD_BM - 1) / FWD_BM;
   std::vector<Item> items;
   for (int t = 0; t < ntiles; ++t) {
-    const int nb = fwd_tile_blocks(N, Nk, t, causal);
+    const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
     int np = 1;
     if (T > 0 && nb > T) np = std::min(4, (nb + T - 1) / T);
     for (int part = 0; part < np; ++part) {
@@ -143,7 +143,7 @@ std::vector<Item> make_items(int N, int Nk, bool causal, int T) {
   return items;
 }
 
-std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int cus, int occ) {
+std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ) {
   auto plan = std::make_unique<FwdPlan>();
   plan->nitems = 0;
   plan->nslots = 0;
@@ -152,15 +152,15 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int cus,
   if (cus <= 0 || occ <= 0 || ntiles > 0xffff || (long long)BH * ntiles >= kMaxWaves * slots ||
       (long long)BH * ntiles > FWD_COUNTERS)
     return plan;
-  const int nbmax = fwd_tile_blocks(N, Nk, ntiles - 1, causal);
-  const double base = simulate(make_items(N, Nk, causal, 0), BH, cus, occ);
+  const int nbmax = fwd_tile_blocks(N, Nk, ntiles - 1, causal, bn);
+  const double base = simulate(make_items(N, Nk, causal, bn, 0), BH, cus, occ);
   double best = base * kMinGain;
   int bestT = 0;
   static const double fracs[] = {0.875, 0.75, 0.625, 0.5, 0.4, 1.0 / 3.0, 0.25};
   for (double f : fracs) {
     const int T = std::max(4, (int)(nbmax * f + 0.999));
     if (T >= nbmax) continue;
-    const std::vector<Item> items = make_items(N, Nk, causal, T);
+    const std::vector<Item> items = make_items(N, Nk, causal, bn, T);
     if ((int)items.size() > FWD_PLAN_MAX) continue;
     const double ms = simulate(items, BH, cus, occ);
     if (ms < best) {
@@ -169,12 +169,12 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int cus,
     }
   }
   if (bestT == 0) return plan;
-  const std::vector<Item> items = make_items(N, Nk, causal, bestT);
+  const std::vector<Item> items = make_items(N, Nk, causal, bn, bestT);
   // Slot bases: consecutive per split tile, in tile order.
   std::vector<int> base_of(ntiles, 0);
   int nslots = 0;
   for (int t = 0; t < ntiles; ++t) {
-    const int nb = fwd_tile_blocks(N, Nk, t, causal);
+    const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
     const int np = (nb > bestT) ? std::min(4, (nb + bestT - 1) / bestT) : 1;
     base_of[t] = nslots;
     if (np > 1) nslots += np;
@@ -193,14 +193,14 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int cus,
 
 }  // namespace
 
-const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int cus, int occ) {
+const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ) {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, int, bool, int, int>, std::unique_ptr<FwdPlan>> cache;
+  static std::map<std::tuple<int, int, int, bool, int, int, int>, std::unique_ptr<FwdPlan>> cache;
   std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_tuple(N, Nk, BH, causal, cus, occ);
+  auto key = std::make_tuple(N, Nk, BH, causal, bn, cus, occ);
   auto it = cache.find(key);
   if (it != cache.end()) return *it->second;
-  auto res = cache.emplace(key, build_plan(N, Nk, BH, causal, cus, occ));
+  auto res = cache.emplace(key, build_plan(N, Nk, BH, causal, bn, cus, occ));
   return *res.first->second;
 }
 

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_OK = 0,
@@ -198,17 +198,19 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
 
 /*
  * Host-only view of fa_fwd_ex's work plan (no device call): for Nq query
- * rows and Nk keys, BH = B*H query heads, mask_kind, `cus` compute units and
- * `occ` resident
- * workgroups per compute unit, returns the number of work items (0 = one
- * item per query tile, no split) and copies up to max_items of them to
- * `items`, each
+ * rows and Nk keys, BH = B*H query heads, head dimension d, mask_kind, `cus`
+ * compute units and `occ` resident workgroups per compute unit, returns the
+ * number of work items (0 = one item per query tile, no split) and copies up
+ * to max_items of them to `items`, each
  *   tile | part << 16 | (nparts - 1) << 18 | slot_base << 20,
  * in dispatch order; *nslots receives the partial-state slots per head.
+ * Query tiles are 128 rows; a tile's keys stream in blocks of 64 keys for
+ * d <= 64 and of 32 above, and part p of n covers blocks
+ * [p * nb / n, (p + 1) * nb / n) of the tile's nb blocks.
  * Returns FA_ERR_INVALID_ARG for invalid arguments.
  */
-int fa_fwd_schedule(int Nq, int Nk, int BH, int mask_kind, int cus, int occ, uint32_t* items,
-                    int max_items, int* nslots);
+int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int occ,
+                    uint32_t* items, int max_items, int* nslots);
 
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);

@@ -1,9 +1,10 @@
 """fa_fwd_ex's host-side work plan (fa_fwd_schedule; no device involved).
 
 Every query tile must be covered exactly once: its nominal key blocks
-(ceil(min(Nk, 128 (t+1) + Nk - Nq) / 32) under the causal mask, the queries
-being the last Nq of Nk positions; ceil(Nk / 32) without) are partitioned by
-the parts of the tile, split tiles own disjoint
+(ceil(min(Nk, 128 (t+1) + Nk - Nq) / bn) under the causal mask, the queries
+being the last Nq of Nk positions; ceil(Nk / bn) without; bn = 64 keys for
+head dimensions up to 64, 32 above) are partitioned by the parts of the tile,
+split tiles own disjoint
 partial-state slots, and the items come longest first under the planner's
 stated cost model. The schedule simulation that chose the plan is
 re-implemented here from its description (compute units of `occ` slots whose
@@ -18,15 +19,19 @@ import pytest
 
 from exact_io_aware_17_amd import _lib
 
-BM, BN = 128, 32
+BM = 128
+
+
+def block_keys(d):
+    return 64 if d <= 64 else 32
 ITEM, SPLIT = 2.0, 7.0   # cost per item and extra per split part, in key blocks
 MIN_GAIN = 0.75
 
 
-def tile_blocks(N, t, causal, Nk=None):
+def tile_blocks(N, t, causal, Nk=None, d=128):
     Nk = N if Nk is None else Nk
     kend = max(0, min(Nk, BM * (t + 1) + Nk - N)) if causal else Nk
-    return math.ceil(kend / BN)
+    return math.ceil(kend / block_keys(d))
 
 
 def decode(item):
@@ -77,7 +82,7 @@ def simulate(costs, BH, cus, occ):
     return end
 
 
-# (Nq, Nk, BH, causal, cus, occ)
+# (Nq, Nk, BH, causal, cus, occ[, d])
 CASES = [
     (4096, 4096, 32, True, 256, 3),     # the metric shape: several waves of work, not split
     (4096, 4096, 32, False, 256, 3),
@@ -94,21 +99,25 @@ CASES = [
     (16, 8192, 8, False, 256, 3),
     (1024, 8192, 4, True, 256, 3),      # a continuation after a 7168-key prefix
     (2048, 1000, 2, True, 256, 3),      # Nq > Nk: early query tiles see no key
+    (16384, 16384, 2, True, 256, 3, 64),  # 64-key blocks (d <= 64)
+    (4096, 4096, 4, False, 256, 3, 32),
+    (1, 32768, 8, True, 256, 3, 64),
 ]
+CASES = [c if len(c) == 7 else c + (128,) for c in CASES]
 
 
-def _costs(items, N, Nk, causal):
+def _costs(items, N, Nk, causal, d=128):
     out = []
     for it in items:
         t, part, np_, _ = decode(it)
-        nb = tile_blocks(N, t, causal, Nk)
+        nb = tile_blocks(N, t, causal, Nk, d)
         out.append((part + 1) * nb // np_ - part * nb // np_ + ITEM + (SPLIT if np_ > 1 else 0))
     return out
 
 
-@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ", CASES)
-def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ):
-    items, nslots = _lib.schedule(N, BH, causal, cus, occ, Nk)
+@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ,d", CASES)
+def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ, d):
+    items, nslots = _lib.schedule(N, BH, causal, cus, occ, Nk, d)
     ntiles = math.ceil(N / BM)
     if not items:
         return
@@ -125,7 +134,7 @@ def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ):
         np_ = ps[0][1]
         assert sorted(p for p, _, _ in ps) == list(range(np_))
         assert all(n == np_ for _, n, _ in ps)
-        nb = tile_blocks(N, t, causal, Nk)
+        nb = tile_blocks(N, t, causal, Nk, d)
         ranges = sorted((p * nb // np_, (p + 1) * nb // np_) for p, _, _ in ps)
         assert ranges[0][0] == 0 and ranges[-1][1] == nb
         assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
@@ -139,15 +148,16 @@ def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ):
             assert sb + np_ <= nslots
 
 
-@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ", CASES)
-def test_plan_is_longest_first_and_pays_off(N, Nk, BH, causal, cus, occ):
-    items, _ = _lib.schedule(N, BH, causal, cus, occ, Nk)
+@pytest.mark.parametrize("N,Nk,BH,causal,cus,occ,d", CASES)
+def test_plan_is_longest_first_and_pays_off(N, Nk, BH, causal, cus, occ, d):
+    items, _ = _lib.schedule(N, BH, causal, cus, occ, Nk, d)
     if not items:
         return
-    costs = _costs(items, N, Nk, causal)
+    costs = _costs(items, N, Nk, causal, d)
     assert all(a >= b for a, b in zip(costs, costs[1:]))
     ntiles = math.ceil(N / BM)
-    unsplit = sorted((tile_blocks(N, t, causal, Nk) + ITEM for t in range(ntiles)), reverse=True)
+    unsplit = sorted((tile_blocks(N, t, causal, Nk, d) + ITEM for t in range(ntiles)),
+                     reverse=True)
     assert simulate(costs, BH, cus, occ) < MIN_GAIN * simulate(unsplit, BH, cus, occ)
 
 
@@ -166,10 +176,11 @@ def test_split_only_underfilled_grids():
 def test_schedule_argument_errors():
     lib = _lib.load()
     INV = _lib.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_schedule(0, 128, 1, 1, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 0, 1, 1, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 128, 0, 1, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 128, 1, 5, 256, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 128, 1, 1, -1, 3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 128, 1, 1, 256, -3, None, 0, None) == INV
-    assert lib.fa_fwd_schedule(128, 128, 1, 1, 256, 3, None, 4, None) == INV
+    assert lib.fa_fwd_schedule(0, 128, 1, 128, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 0, 1, 128, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 0, 128, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 0, 1, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 128, 5, 256, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, -1, 3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, 256, -3, None, 0, None) == INV
+    assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, 256, 3, None, 4, None) == INV

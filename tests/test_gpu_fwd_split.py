@@ -22,9 +22,9 @@ DEV = "cuda:0"
 # (B, H, N, d, causal, kv_lens)
 CASES = [
     (1, 1, 1024, 128, False, None),       # every tile in 4 parts
-    (1, 2, 768, 64, True, [700]),
+    (1, 2, 1536, 64, True, [1400]),       # 64-key blocks (d = 64)
     (2, 3, 1000, 128, True, None),        # ragged last tile
-    (2, 2, 640, 64, False, [0, 333]),     # an empty batch and parts beyond kv_len
+    (2, 2, 1024, 64, False, [0, 333]),    # an empty batch and parts beyond kv_len
     (1, 2, 4096, 128, True, None),
     (2, 1, 2048, 128, True, [2048, 700]),
     (1, 2, 2048, 128, "strict", None),    # row 0 of every head sees no key
