@@ -299,10 +299,33 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
     f32x16 s, dp;
     zero(s);
     zero(dp);
+    if constexpr (D <= 128) {
+      // All K operand reads first, then the S^T products with the V operand
+      // reads in between, then dP^T: one LDS latency ahead of the matrix
+      // work instead of one per pair of reads (the scheduler alone keeps two
+      // reads in flight). At D = 256 the operands would not fit the registers.
+      x8 kop[DC], vop[DC];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      s = E::mfma(*(const x8*)(ks + off.roff[c]), qf[c], s);
-      dp = E::mfma(*(const x8*)(vs + off.roff[c]), of[c], dp);
+      for (int c = 0; c < DC; ++c) kop[c] = *(const x8*)(ks + off.roff[c]);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) vop[c] = *(const x8*)(vs + off.roff[c]);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) s = E::mfma(kop[c], qf[c], s);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) dp = E::mfma(vop[c], of[c], dp);
+      __builtin_amdgcn_sched_group_barrier(0x100, DC, 0);  // DS reads (K)
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA (S^T)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read (V)
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, DC, 0);  // MFMAs (dP^T)
+    } else {
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        s = E::mfma(*(const x8*)(ks + off.roff[c]), qf[c], s);
+        dp = E::mfma(*(const x8*)(vs + off.roff[c]), of[c], dp);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa + shift);
