@@ -361,7 +361,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "fwd_kernel<__bf16, 128, 32, 2, true>",
+            "kernel": f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, 2, "
+                      f"{'true' if w.causal else 'false'}>",
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_kernel, 5),
             "kernel_ms_min": round(per_launch[0], 5),

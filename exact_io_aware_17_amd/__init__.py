@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     FA_MASK_NONE,
     FA_OK,
     FaError,
+    block_keys,
     bwd,
     bwd_workspace_bytes,
     default_scale,

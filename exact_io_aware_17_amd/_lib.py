@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -45,6 +45,7 @@ SIGNATURES = {
     "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "fa_fwd_block_keys": (_i, [_i, _i, _i, _i, _i, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
 }
@@ -267,6 +268,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
                                ws_ptr, ws_bytes, stream)
     _check(fn_name, st)
     return out, lse
+
+
+def block_keys(B: int, H: int, N: int, d: int, causal=False, Nk: Optional[int] = None) -> int:
+    """fa_fwd_block_keys: keys per streamed block of the forward launch on the
+    current device."""
+    n = int(load().fa_fwd_block_keys(B, H, N, N if Nk is None else Nk, d, mask_kind(causal)))
+    if n < 0:
+        raise FaError("fa_fwd_block_keys", n, status_string(n))
+    return n
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

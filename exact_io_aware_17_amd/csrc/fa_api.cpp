@@ -105,17 +105,18 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.counters = nullptr;
   p.part_ml = nullptr;
   p.part_o = nullptr;
+  p.bn = 0;
   if (f32) {
     hipError_t e = fa::launch_fwd_f32(p, (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
+  const int BH = B * H;
+  const int cus = fa::fwd_device_cus();
+  p.bn = fa::fwd_block_keys(d, Nq, Nk, BH, p.causal != 0, cus);
   const fa::FwdPlan* plan = &no_plan();
   if (workspace) {
-    const int BH = B * H;
-    int cus = 0, occ = 0;
-    fa::fwd_occupancy(d, p.causal != 0, p.dtype, &cus, &occ);
-    const fa::FwdPlan& cand =
-        fa::fwd_plan(Nq, Nk, BH, p.causal != 0, fa::fwd_block_keys(d), cus, occ);
+    const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
+    const fa::FwdPlan& cand = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, Nq, d);
     if (cand.nitems > 0 && workspace_bytes >= w.total) {
       plan = &cand;
@@ -218,9 +219,10 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
   if (check_common(B, H, Hkv, Nq, Nk, d, 1.f, mask_kind) != FA_OK) return 0;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return 0;  // fp32: never split
   const bool causal = (mask_kind != FA_MASK_NONE);
-  int cus = 0, occ = 0;
-  fa::fwd_occupancy(d, causal, dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16, &cus, &occ);
-  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, fa::fwd_block_keys(d), cus, occ);
+  const int cus = fa::fwd_device_cus();
+  const int bn = fa::fwd_block_keys(d, Nq, Nk, B * H, causal, cus);
+  const int occ = fa::fwd_occupancy(d, bn, causal, dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16);
+  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, bn, cus, occ);
   return fa::fwd_workspace_layout(plan, B * H, Nq, d).total;
 }
 
@@ -245,11 +247,18 @@ int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int o
   if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
       mask_kind != FA_MASK_CAUSAL_STRICT)
     return FA_ERR_INVALID_ARG;
+  const bool causal = mask_kind != FA_MASK_NONE;
   const fa::FwdPlan& plan =
-      fa::fwd_plan(Nq, Nk, BH, mask_kind != FA_MASK_NONE, fa::fwd_block_keys(d), cus, occ);
+      fa::fwd_plan(Nq, Nk, BH, causal, fa::fwd_block_keys(d, Nq, Nk, BH, causal, cus), cus, occ);
   for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
   if (nslots) *nslots = plan.nslots;
   return plan.nitems;
+}
+
+int fa_fwd_block_keys(int B, int H, int Nq, int Nk, int d, int mask_kind) {
+  const int st = check_common(B, H, H, Nq, Nk, d, 1.f, mask_kind);
+  if (st != FA_OK) return st;
+  return fa::fwd_block_keys(d, Nq, Nk, B * H, mask_kind != FA_MASK_NONE, fa::fwd_device_cus());
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

@@ -87,14 +87,17 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 #endif
 
 // Resident workgroups per CU the register budget is sized for: at D = 256 the
-// Q^T fragments and output accumulators alone take 192 registers per lane.
-constexpr int fwd_wg_per_cu(int D) { return D == 256 ? 1 : FA_FWD_WG_PER_CU; }
+// Q^T fragments and output accumulators alone take 192 registers per lane;
+// 64-key blocks at D = 128 hold two score tiles (210 registers).
+constexpr int fwd_wg_per_cu(int D, int BN) {
+  return D == 256 ? 1 : (D == 128 && BN == 64 ? 2 : FA_FWD_WG_PER_CU);
+}
 
 // Head dimensions with kernel instances.
 #define FA_FOR_EACH_D(X) X(32) X(64) X(96) X(128) X(256)
 
 template <typename T, int D, int BN, int STAGES, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParams p, FwdPlan plan) {
+__global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdParams p, FwdPlan plan) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
   constexpr int ROWB = D * 2;                 // bytes per K/V row
@@ -491,9 +494,9 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D)) void fwd_kernel(FwdParam
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int BN>
 hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-  constexpr int BN = fwd_block_keys(D), ST = FA_FWD_STAGES;  // the planner counts these blocks
+  constexpr int ST = FA_FWD_STAGES;
   const long long ntiles = (p.N + BM - 1) / BM;
   const long long items = plan.nitems > 0 ? plan.nitems : ntiles;
   const long long grid = (long long)p.B * p.H * items;
@@ -507,59 +510,94 @@ hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream)
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL>
 int occupancy() {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, fwd_block_keys(D), FA_FWD_STAGES, CAUSAL>),
-          NW * 64, 0) != hipSuccess)
+          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, BN, FA_FWD_STAGES, CAUSAL>), NW * 64,
+          0) != hipSuccess)
     return 0;
   return per;
 }
 
-template <typename T>
-int occupancy_of(int d, bool causal) {
-#define FA_OCC(DD) \
-  if (d == DD) return causal ? occupancy<T, DD, true>() : occupancy<T, DD, false>();
-  FA_FOR_EACH_D(FA_OCC)
-#undef FA_OCC
-  return 0;
+// Calls f(std::integral_constant<int, BN>) for the block sizes instantiated
+// at head dimension D (64 at D <= 64; 32 and 64 at D = 128; 32 otherwise);
+// returns `fallback` for any other bn.
+template <int D, typename F, typename R>
+R with_block_keys(int bn, F&& f, R fallback) {
+  if constexpr (D <= 64) {
+    if (bn == 64) return f(std::integral_constant<int, 64>());
+  } else if constexpr (D == 128) {
+    if (bn == 32) return f(std::integral_constant<int, 32>());
+    if (bn == 64) return f(std::integral_constant<int, 64>());
+  } else {
+    if (bn == 32) return f(std::integral_constant<int, 32>());
+  }
+  return fallback;
+}
+
+template <typename T, int D>
+int occupancy_of(int bn, bool causal) {
+  return with_block_keys<D>(bn, [&](auto b) {
+    constexpr int BN = decltype(b)::value;
+    return causal ? occupancy<T, D, BN, true>() : occupancy<T, D, BN, false>();
+  }, 0);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-#define FA_LAUNCH(DD)                                            \
-  if (p.d == DD) {                                               \
-    if (p.dtype == DTYPE_BF16) return launch_d<__bf16, DD>(p, plan, stream);   \
-    if (p.dtype == DTYPE_F16) return launch_d<_Float16, DD>(p, plan, stream);  \
+#define FA_LAUNCH(DD)                                                                    \
+  if (p.d == DD) {                                                                       \
+    return with_block_keys<DD>(p.bn, [&](auto b) {                                       \
+      constexpr int BN = decltype(b)::value;                                             \
+      if (p.dtype == DTYPE_BF16) return launch_d<__bf16, DD, BN>(p, plan, stream);       \
+      if (p.dtype == DTYPE_F16) return launch_d<_Float16, DD, BN>(p, plan, stream);      \
+      return hipErrorInvalidValue;                                                       \
+    }, hipErrorInvalidValue);                                                            \
   }
   FA_FOR_EACH_D(FA_LAUNCH)
 #undef FA_LAUNCH
   return hipErrorInvalidValue;
 }
 
-void fwd_occupancy(int d, bool causal, int dtype, int* cus_out, int* occ_out) {
+int fwd_device_cus() {
   static std::mutex mu;
-  static std::map<std::tuple<int, int, bool, int>, std::pair<int, int>> cache;
-  *cus_out = 0;
-  *occ_out = 0;
+  static std::map<int, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_tuple(dev, d, causal, dtype);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 0)
+      cus = 0;
+    it = cache.emplace(dev, cus).first;
+  }
+  return it->second;
+}
+
+int fwd_occupancy(int d, int bn, bool causal, int dtype) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, bool, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, d, bn, causal, dtype);
   auto it = cache.find(key);
   if (it == cache.end()) {
-    int cus = 0, per = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 0;
-    if (dtype == DTYPE_BF16) per = occupancy_of<__bf16>(d, causal);
-    if (dtype == DTYPE_F16) per = occupancy_of<_Float16>(d, causal);
-    if (cus <= 0 || per <= 0) cus = per = 0;
-    it = cache.emplace(key, std::make_pair(cus, per)).first;
+    int per = 0;
+#define FA_OCC(DD)                                                      \
+  if (d == DD) {                                                        \
+    if (dtype == DTYPE_BF16) per = occupancy_of<__bf16, DD>(bn, causal);   \
+    if (dtype == DTYPE_F16) per = occupancy_of<_Float16, DD>(bn, causal);  \
   }
-  *cus_out = it->second.first;
-  *occ_out = it->second.second;
+    FA_FOR_EACH_D(FA_OCC)
+#undef FA_OCC
+    it = cache.emplace(key, per > 0 ? per : 0).first;
+  }
+  return it->second;
 }
 
 }  // namespace fa

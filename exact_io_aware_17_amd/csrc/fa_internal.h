@@ -20,6 +20,7 @@ struct FwdParams {
   int B, H, N, d;          // N: query rows per head
   int Hkv, Nk;             // K/V heads (a divisor of H) and key rows per head
   int dtype;               // DTYPE_*
+  int bn;                  // keys per streamed block (fwd_block_keys), 16-bit paths
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
   int causal;              // key j visible to query i only if j <= i + Nk - N - diag
@@ -35,10 +36,13 @@ struct FwdParams {
 
 // Forward tiling shared by the kernel and the host planner.
 constexpr int FWD_BM = 128;                 // query rows per workgroup
-// Keys per streamed block: 64 for head dimensions up to 64 (each block's
-// fixed costs, its barrier and its softmax bookkeeping, then meet as much
-// matrix work as a 32-key block at d = 128), 32 above.
-constexpr int fwd_block_keys(int d) { return d <= 64 ? 64 : 32; }
+// Keys per streamed block of a forward launch (the planner counts these
+// blocks): 64 for head dimensions up to 64; at d = 128, 64 (two workgroups
+// per CU) without the causal mask or for long causal rows on at most two
+// waves of workgroups, else 32 (three per CU); 32 at d = 96 and 256.
+int fwd_block_keys(int d, int Nq, int Nk, int BH, bool causal, int cus);
+// Compute units of the current device (0 if unknown; cached).
+int fwd_device_cus();
 constexpr int FWD_ML_FLOATS = 4 * 2 * FWD_BM;  // {m, l, l_bf, 0} for each of 2*BM lanes
 constexpr int FWD_PLAN_MAX = 512;
 // Arrival counters occupy a fixed region at the start of every forward
@@ -69,9 +73,9 @@ struct FwdWorkspace {
   size_t counters, part_ml, part_o, total;
 };
 FwdWorkspace fwd_workspace_layout(const FwdPlan& plan, int BH, int N, int d);
-// Compute units of the current device and resident forward workgroups per
-// compute unit for head dimension d and element type dtype (both 0 if unknown).
-void fwd_occupancy(int d, bool causal, int dtype, int* cus, int* occ);
+// Resident forward workgroups per compute unit of the instance for head
+// dimension d, block size bn and element type dtype (0 if unknown; cached).
+int fwd_occupancy(int d, int bn, bool causal, int dtype);
 
 struct BwdParams {
   const void* q;

@@ -200,3 +200,17 @@ def test_bwd_ex_argument_errors():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+def test_block_keys_rule_and_errors():
+    lib = _lib.load()
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_block_keys(0, 1, 16, 16, 64, 0) == INV
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 64, 9) == INV
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 80, 0) == UNS
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 32, 1) == 64
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 64, 1) == 64
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 96, 0) == 32
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 0) == 64   # no mask: 64 at d = 128
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 1) == 32   # short causal rows
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 256, 0) == 32

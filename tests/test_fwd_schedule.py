@@ -2,8 +2,8 @@
 
 Every query tile must be covered exactly once: its nominal key blocks
 (ceil(min(Nk, 128 (t+1) + Nk - Nq) / bn) under the causal mask, the queries
-being the last Nq of Nk positions; ceil(Nk / bn) without; bn = 64 keys for
-head dimensions up to 64, 32 above) are partitioned by the parts of the tile,
+being the last Nq of Nk positions; ceil(Nk / bn) without; bn, the keys per
+block, as the header documents) are partitioned by the parts of the tile,
 split tiles own disjoint
 partial-state slots, and the items come longest first under the planner's
 stated cost model. The schedule simulation that chose the plan is
@@ -22,16 +22,24 @@ from exact_io_aware_17_amd import _lib
 BM = 128
 
 
-def block_keys(d):
-    return 64 if d <= 64 else 32
+def block_keys(d, Nq, Nk, BH, causal, cus):
+    """Keys per block of the forward launch (the header's rule)."""
+    if d <= 64:
+        return 64
+    if d != 128:
+        return 32
+    if not causal:
+        return 64
+    tiles = BH * math.ceil(Nq / BM)
+    return 64 if (Nk >= 4096 and cus > 0 and tiles <= 4 * cus) else 32
 ITEM, SPLIT = 2.0, 7.0   # cost per item and extra per split part, in key blocks
 MIN_GAIN = 0.75
 
 
-def tile_blocks(N, t, causal, Nk=None, d=128):
+def tile_blocks(N, t, causal, Nk=None, bn=32):
     Nk = N if Nk is None else Nk
     kend = max(0, min(Nk, BM * (t + 1) + Nk - N)) if causal else Nk
-    return math.ceil(kend / block_keys(d))
+    return math.ceil(kend / bn)
 
 
 def decode(item):
@@ -106,11 +114,11 @@ CASES = [
 CASES = [c if len(c) == 7 else c + (128,) for c in CASES]
 
 
-def _costs(items, N, Nk, causal, d=128):
+def _costs(items, N, Nk, causal, bn):
     out = []
     for it in items:
         t, part, np_, _ = decode(it)
-        nb = tile_blocks(N, t, causal, Nk, d)
+        nb = tile_blocks(N, t, causal, Nk, bn)
         out.append((part + 1) * nb // np_ - part * nb // np_ + ITEM + (SPLIT if np_ > 1 else 0))
     return out
 
@@ -118,6 +126,7 @@ def _costs(items, N, Nk, causal, d=128):
 @pytest.mark.parametrize("N,Nk,BH,causal,cus,occ,d", CASES)
 def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ, d):
     items, nslots = _lib.schedule(N, BH, causal, cus, occ, Nk, d)
+    bn = block_keys(d, N, Nk, BH, causal, cus)
     ntiles = math.ceil(N / BM)
     if not items:
         return
@@ -134,7 +143,7 @@ def test_plan_covers_every_tile_once(N, Nk, BH, causal, cus, occ, d):
         np_ = ps[0][1]
         assert sorted(p for p, _, _ in ps) == list(range(np_))
         assert all(n == np_ for _, n, _ in ps)
-        nb = tile_blocks(N, t, causal, Nk, d)
+        nb = tile_blocks(N, t, causal, Nk, bn)
         ranges = sorted((p * nb // np_, (p + 1) * nb // np_) for p, _, _ in ps)
         assert ranges[0][0] == 0 and ranges[-1][1] == nb
         assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
@@ -153,10 +162,11 @@ def test_plan_is_longest_first_and_pays_off(N, Nk, BH, causal, cus, occ, d):
     items, _ = _lib.schedule(N, BH, causal, cus, occ, Nk, d)
     if not items:
         return
-    costs = _costs(items, N, Nk, causal, d)
+    bn = block_keys(d, N, Nk, BH, causal, cus)
+    costs = _costs(items, N, Nk, causal, bn)
     assert all(a >= b for a, b in zip(costs, costs[1:]))
     ntiles = math.ceil(N / BM)
-    unsplit = sorted((tile_blocks(N, t, causal, Nk, d) + ITEM for t in range(ntiles)),
+    unsplit = sorted((tile_blocks(N, t, causal, Nk, bn) + ITEM for t in range(ntiles)),
                      reverse=True)
     assert simulate(costs, BH, cus, occ) < MIN_GAIN * simulate(unsplit, BH, cus, occ)
 
