@@ -164,8 +164,10 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
     for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         rows = read(d, counter)
         first_fwd = min((i for i, n, _ in rows if FWD_KERNEL_TAG in n), default=-1)
+        # dispatches before the first forward that moved at least a quarter of
+        # the copy's bytes: the copies (FETCH_SIZE reads about half of them)
         copy = [v for i, n, v in rows
-                if i < first_fwd and FWD_KERNEL_TAG not in n and v > 0.5 * COPY_BYTES / 1024]
+                if i < first_fwd and FWD_KERNEL_TAG not in n and v >= 0.25 * COPY_BYTES / 1024]
         fwd = [v for _, n, v in rows if FWD_KERNEL_TAG in n]
         if not copy or len(fwd) != 3 + len(SWEEP_N):
             print(f"{counter}: expected copy readings and {3 + len(SWEEP_N)} forward "
