@@ -123,6 +123,16 @@ def test_strict_causal(dtype, d, N):
         assert torch.equal(o[:, :, 1], x["v"].to(DEV)[:, :, 0])
 
 
+@pytest.mark.parametrize("causal", [True, "strict"])
+def test_64_key_causal_instance_with_ragged_tail(causal):
+    # Causal rows of at least 4096 keys on a small grid take the 64-key d = 128
+    # instance (rolling transpose-read schedule); N = 4133 leaves a ragged last
+    # block and kv_len 4100 a masked one.
+    w = W.Workload(99, "64-key causal ragged", 2, 2, 4133, 128, "bf16", causal)
+    assert fa.block_keys(w.B, w.H, w.N, w.d, causal) == 64
+    _full_check(w, kv_lens=torch.tensor([4133, 4100], dtype=torch.int32))
+
+
 def test_strict_causal_with_padding():
     w = W.Workload(98, "strict padded", 3, 2, 300, 128, "bf16", "strict")
     _full_check(w, kv_lens=torch.tensor([0, 1, 170], dtype=torch.int32))
