@@ -235,7 +235,8 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
   __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N;
   const int ntiles = (N + BT - 1) / BT;
@@ -328,10 +329,18 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    // Hidden keys (only in blocks that straddle the diagonal or kv_len): the
+    // score becomes -inf, so its P is exactly 0. A uniform branch of its own,
+    // so unmasked blocks pay nothing for it.
     const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa + shift);
-    int lim = kvlen - 1;  // key visible iff key <= lim
-    if (CAUSAL) lim = min(lim, qrow + shift);
-    lim -= key0 + 4 * h;
+    if (need_mask) {
+      int lim = kvlen - 1;  // key visible iff key <= lim
+      if (CAUSAL) lim = min(lim, qrow + shift);
+      lim -= key0 + 4 * h;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = NEG_INF;
+    }
     x8 df[2];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -342,8 +351,7 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int r = 8 * kc + 2 * e + u;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -lse2));
-          if (need_mask && 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -lse2));
           v2[u] = pv * (dp[r] - dl);  // dS^T
         }
         w[e] = E::pack(v2[0], v2[1]);
@@ -397,7 +405,8 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   constexpr bool KF_LDS = (D == 128) && (OUT == (DKDV_V | DKDV_K));
   __shared__ __attribute__((aligned(1024))) char kfl[KF_LDS ? NWB * DC * 1024 : 16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N, Nk = p.Nk;
   const int G = p.H / p.Hkv;  // query heads per K/V head
@@ -485,7 +494,17 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
       s = E::mfma(*(const x8*)(qs + off.roff[c]), kc, s);
     }
     __builtin_amdgcn_s_setprio(0);
+    // Hidden pairs (only in blocks that straddle the diagonal, kv_len or the
+    // last query row): the score becomes -inf, so its P is exactly 0. A
+    // uniform branch of its own, so unmasked blocks pay nothing for it.
     const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0 + shift);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int query = qb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= kvlen || query >= N || (CAUSAL && key > query + shift)) s[r] = NEG_INF;
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int ql = 8 * g + 4 * h;  // four consecutive queries of this lane
@@ -493,12 +512,7 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[e]));
-        if (need_mask) {
-          const int query = qb0 + ql + e;
-          if (key >= kvlen || query >= N || (CAUSAL && key > query + shift)) pr = 0.f;
-        }
-        s[r] = pr;  // P, fp32
+        s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[e]));  // P, fp32
       }
     }
     x8 pf[2];
