@@ -339,10 +339,10 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // ---- online softmax ----
     // Probabilities against the current reference max m_run. While the
     // block's row max stays within TAU of it every p is at most 2^TAU, so a
-    // lane sum above 2^TAU (or not a number: m_run = -inf at the start) is
-    // the only case that needs the block max: then the reference moves to
-    // the row's block max if that lies more than TAU above it (rescaling the
-    // accumulators once), and the block's p are recomputed.
+    // lane sum above 2^TAU (or not a number: a row whose keys were all
+    // hidden so far) is the only case that needs the block max: then the
+    // reference moves to the row's block max if that lies more than TAU above
+    // it (rescaling the accumulators once), and the block's p are recomputed.
     x8 pf[KC];
     float rs, lbf_blk;
     auto probabilities = [&](float m_use) {
@@ -363,7 +363,20 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
         pf[kc] = __builtin_bit_cast(x8, w);
       }
     };
-    probabilities(m_run);
+    if (j == jbeg) {
+      // First block of the item: there is nothing to rescale yet, so the
+      // reference max is simply the block's row max (-inf for a row with no
+      // visible key, whose p are then 0) and the lag check below passes.
+      float mx = NEG_INF;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      m_run = pair_max(mx) * scl;
+      probabilities((m_run == NEG_INF) ? 0.f : m_run);
+    } else {
+      probabilities(m_run);
+    }
     if (__any(!(rs <= P_BOUND))) {
       float mx = NEG_INF;
 #pragma unroll
