@@ -453,10 +453,11 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   const int qstart = CAUSAL ? min(max(kb0 - shift, 0) / BS, nqb) : 0;
   const int nq = nqb - qstart;
   const int nsteps = (kb0 < kvlen) ? G * nq : 0;  // every key of the tile hidden: nothing to do
-  auto issue = [&](int u, auto stage) {
+  // Step u streams query block i of group head g (u = g * nq + i - qstart);
+  // (i, g) advance with u, so no step divides by nq.
+  auto issue = [&](int u, int i, int g, auto stage) {
     constexpr int SD = decltype(stage)::value;
     if (u >= nsteps) return;
-    const int g = u / nq, i = qstart + u % nq;
     const size_t qh = qhead0 + g;
     issue_tiles<D>((const T*)p.q + qh * N * D, (const T*)p.dout + qh * N * D, i * BS, N,
                    SD == 0 ? qbuf0 : qbuf1, SD == 0 ? obuf0 : obuf1, wave, lane);
@@ -467,12 +468,20 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     }
   };
   // Step u uses stage u % 2; unrolled by the two stages as in the dQ kernel.
+  int cur_i = qstart, cur_g = 0;  // block of the current step
   auto step = [&](int u, auto stage) {
     constexpr int ST = decltype(stage)::value;
     wait_vmem();
     __syncthreads();
-    issue(u + 1, std::integral_constant<int, 1 - ST>());
-    const int qb0 = (qstart + u % nq) * BS;
+    const int qb0 = cur_i * BS;
+    int ni = cur_i + 1, ng = cur_g;
+    if (ni == nqb) {
+      ni = qstart;
+      ++ng;
+    }
+    issue(u + 1, ni, ng, std::integral_constant<int, 1 - ST>());
+    cur_i = ni;
+    cur_g = ng;
     if (kw0 >= kvlen) return;                         // all of this wave's keys are hidden
     if (CAUSAL && kw0 > qb0 + BS - 1 + shift) return;  // every query of the block precedes them
     const char* qs = ST == 0 ? qbuf0 : qbuf1;
@@ -563,7 +572,7 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
       for (int qc = 0; qc < 2; ++qc) dka[dt] = E::mfma(tr_operand<x8, D>(qs, off, dt, qc), df[qc], dka[dt]);
     __builtin_amdgcn_s_setprio(0);
   };
-  issue(0, std::integral_constant<int, 0>());
+  issue(0, qstart, 0, std::integral_constant<int, 0>());
   for (int u = 0; u < nsteps; u += 2) {
     step(u, std::integral_constant<int, 0>());
     if (u + 1 < nsteps) step(u + 1, std::integral_constant<int, 1>());
