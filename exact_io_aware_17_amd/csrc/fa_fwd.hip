@@ -300,11 +300,10 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // barrier, which also frees the other stage, read in block j-1.
     wait_vmem();
     __syncthreads();
-    issue_block(j + 1, std::integral_constant<int, 1 - ST>());
-
     const int key0 = j * BN;
-    // Skip blocks wholly in this wave's future (all its rows would be masked).
-    if (CAUSAL && key0 > qa + 31 + shift) return;
+    // Blocks wholly in this wave's future (all its rows would be masked) are
+    // skipped; the wave still issues its share of the next block's DMA.
+    const bool skip = CAUSAL && key0 > qa + 31 + shift;
     const char* ks = ST == 0 ? kbuf0 : kbuf1;
     const char* vs = ST == 0 ? vbuf0 : vbuf1;
 
@@ -312,16 +311,33 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // Waves in a matrix phase get issue priority over waves in their softmax,
     // so whichever wave has MFMAs ready keeps the matrix pipe fed while the
     // others' VALU work fills the gaps.
-    __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
     f32x16 s[KT];
+    if (!skip) {
+      __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) zero(s[t]);
+      for (int t = 0; t < KT; ++t) zero(s[t]);
 #pragma unroll
-    for (int c = 0; c < DC; ++c)
+      for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-        s[t] = E::mfma(*(const x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
-
+        for (int t = 0; t < KT; ++t)
+          s[t] = E::mfma(*(const x8*)(ks + t * 32 * ROWB + koff[c]), qf[c], s[t]);
+      if constexpr (D == 128 && BN == 64) {
+        // Rolling read-ahead: the K reads of chunk c+1 go out before the
+        // MFMAs of chunk c, so each wait leaves two reads in flight.
+        __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);  // DS reads
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          if (c + 1 < DC) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);  // MFMA
+        }
+      }
+    }
+    // The next block's DMA goes out after the S products are issued: its
+    // issue overlaps their drain instead of delaying the first K read, and
+    // with no LDS DMA in flight during the K reads the compiler waits for
+    // each read by count (lgkmcnt(n)) rather than for all of them.
+    issue_block(j + 1, std::integral_constant<int, 1 - ST>());
+    if (skip) return;
     __builtin_amdgcn_s_setprio(0);
     // ---- mask (only blocks that straddle the diagonal or kv_len) ----
     const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa + shift);
