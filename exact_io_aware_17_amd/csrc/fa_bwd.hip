@@ -119,21 +119,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 
 // DMA of rows [r0, r0 + BS) of two row-major [N, D] 16-bit matrices X0, X1
 // into LDS tiles dst0, dst1 (rows past N repeat row N-1; they are masked by
-// the callers). Each DMA fills 1 KB (64 lanes x 16 bytes) of a tile. Where a
-// tile splits into whole rows per DMA and evenly over the waves (D = 64, 128,
-// 256), every wave loads its share of both tiles; otherwise (D = 32, 96) the
-// DMAs of both tiles form one list dealt round-robin over the waves, lane l
-// of DMA b covering slot 64 b + l of its tile in row-major order.
+// the callers; r0 < N). Each DMA fills 1 KB (64 lanes x 16 bytes) of a tile
+// with a buffer load into LDS from a resource based at row r0 (a 32-bit
+// per-lane offset, no vector address arithmetic; the compiler counts these
+// only in vmcnt, so LDS operand reads are still waited for by count). Where
+// a tile splits into whole rows per DMA and evenly over the waves (D = 64,
+// 128, 256), every wave loads its share of both tiles; otherwise (D = 32,
+// 96) the DMAs of both tiles form one list dealt round-robin over the waves,
+// lane l of DMA b covering slot 64 b + l of its tile in row-major order.
 template <int D>
 __device__ __forceinline__ void issue_tiles(const void* __restrict__ X0v,
                                             const void* __restrict__ X1v, int r0, int N,
                                             char* dst0, char* dst1, int wave, int lane) {
-  const unsigned short* __restrict__ X0 = (const unsigned short*)X0v;
-  const unsigned short* __restrict__ X1 = (const unsigned short*)X1v;
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
   constexpr int DMA_PER_TILE = BS * ROWB / 1024;
   static_assert((2 * DMA_PER_TILE) % NWB == 0, "the DMAs of two tiles split evenly over the waves");
+  const buffer_rsrc b0 = make_rsrc((const char*)X0v + (size_t)r0 * ROWB);
+  const buffer_rsrc b1 = make_rsrc((const char*)X1v + (size_t)r0 * ROWB);
+  const int last = N - 1 - r0;  // last row of the matrix, relative to r0
   if constexpr (1024 % ROWB == 0 && DMA_PER_TILE % NWB == 0) {
     constexpr int DPW = DMA_PER_TILE / NWB;
     constexpr int ROWS_PER_DMA = 1024 / ROWB;
@@ -141,17 +145,9 @@ __device__ __forceinline__ void issue_tiles(const void* __restrict__ X0v,
     for (int e = 0; e < DPW; ++e) {
       const int blk = wave * DPW + e;
       const int row = blk * ROWS_PER_DMA + lane / CPR;
-      const int pch = lane % CPR;
-      const size_t src = (size_t)min(r0 + row, N - 1);
-      dma16(X0 + src * D + tchunk<D>(row, pch) * 8, dst0 + blk * 1024);
-    }
-#pragma unroll
-    for (int e = 0; e < DPW; ++e) {
-      const int blk = wave * DPW + e;
-      const int row = blk * ROWS_PER_DMA + lane / CPR;
-      const int pch = lane % CPR;
-      const size_t src = (size_t)min(r0 + row, N - 1);
-      dma16(X1 + src * D + tchunk<D>(row, pch) * 8, dst1 + blk * 1024);
+      const int off = min(row, last) * ROWB + tchunk<D>(row, lane % CPR) * 16;
+      dma16_buf(b0, off, dst0 + blk * 1024);
+      dma16_buf(b1, off, dst1 + blk * 1024);
     }
   } else {
 #pragma unroll
@@ -161,9 +157,8 @@ __device__ __forceinline__ void issue_tiles(const void* __restrict__ X0v,
       const int blk = second ? e - DMA_PER_TILE : e;
       const int g = 64 * blk + lane;
       const int row = g / CPR;
-      const size_t src = (size_t)min(r0 + row, N - 1);
-      dma16((second ? X1 : X0) + src * D + tchunk<D>(row, g % CPR) * 8,
-            (second ? dst1 : dst0) + blk * 1024);
+      const int off = min(row, last) * ROWB + tchunk<D>(row, g % CPR) * 16;
+      dma16_buf(second ? b1 : b0, off, (second ? dst1 : dst0) + blk * 1024);
     }
   }
 }
@@ -462,9 +457,13 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     issue_tiles<D>((const T*)p.q + qh * N * D, (const T*)p.dout + qh * N * D, i * BS, N,
                    SD == 0 ? qbuf0 : qbuf1, SD == 0 ? obuf0 : obuf1, wave, lane);
     if (wave == 0) {  // 32 lse*log2(e) then 32 D values, 4 bytes per lane
-      const int qi = min(i * BS + (lane & 31), N - 1);
-      const float* src = ((lane < 32) ? p.lse2 : p.delta) + qh * N + qi;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(SD == 0 ? stat0 : stat1), 4, 0, 0);
+      const size_t row0 = qh * N + (size_t)i * BS;  // the block's first row
+      const int off = min(lane & 31, N - 1 - i * BS) * 4;
+      float* dst = SD == 0 ? stat0 : stat1;
+      if (lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.lse2 + row0), (lds_void*)dst, 4, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(p.delta + row0), (lds_void*)dst, 4, off, 0, 0, 0);
     }
   };
   // Step u uses stage u % 2; unrolled by the two stages as in the dQ kernel.

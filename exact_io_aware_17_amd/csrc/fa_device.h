@@ -108,13 +108,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16-byte global -> LDS copy that bypasses registers (global_load_lds_dwordx4).
-// `lds` must be the same for the whole wave: lane l's 16 bytes land at
-// lds + 16 * l. Completion is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds, 16, 0, 0);
-}
-
 // s_waitcnt vmcnt(0): this wave's outstanding global loads (and LDS DMAs) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -193,6 +186,13 @@ __device__ __forceinline__ void store_coherent16(f32x4 v, buffer_rsrc r, int byt
 }
 __device__ __forceinline__ f32x4 load_coherent16(buffer_rsrc r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CPOL_SC1);
+}
+
+// 16-byte buffer load into LDS (buffer_load_dwordx4 ... lds): lane l's 16
+// bytes at byte offset voff of the resource land at lds + 16 * l. `lds`
+// must be the same for the whole wave; completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16_buf(buffer_rsrc r, int voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void zero(f32x16& x) {

@@ -23,9 +23,9 @@
 //    permits. A = V^T is read from the row-major V tile with the gfx950
 //    transpose read (ds_read_b64_tr_b16): four lanes reading four key rows
 //    give each lane four keys of one d column.
-//  * K and V tiles go from HBM to LDS with direct 16-byte loads (no register
-//    staging) into two buffers: block j+1 is in flight while block j is
-//    used. The 16-byte chunks of a row are permuted per row so the operand
+//  * K and V tiles go from HBM to LDS with 16-byte buffer loads straight
+//    into LDS (no register staging) into two buffers: block j+1 is in flight
+//    while block j is used. The 16-byte chunks of a row are permuted per row so the operand
 //    reads hit every LDS bank evenly. The loop is unrolled by two so that
 //    each buffer's LDS offsets are immediates, and each lane's source offsets
 //    within a block are computed once.
@@ -220,49 +220,45 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
       goff[m] = grow[m] * ROWB + gch[m] * 16;
     }
   }
+  // DMAs are buffer loads with the LDS flag: a per-block buffer resource
+  // (scalar base at the block's first row) and a 32-bit per-lane offset,
+  // so a block costs no vector address arithmetic. Unlike the global form,
+  // these count only in vmcnt for the compiler, which then waits for the
+  // operand reads of the LDS by count while a DMA is in flight.
   auto issue_block = [&](int j, auto stage) {
     constexpr int SD = decltype(stage)::value;
     if (j >= jend) return;
     const int key0 = j * BN;
     char* ks = SD == 0 ? kbuf0 : kbuf1;
     char* vs = SD == 0 ? vbuf0 : vbuf1;
+    const buffer_rsrc kr = make_rsrc(K + (size_t)key0 * D);
+    const buffer_rsrc vr = make_rsrc(V + (size_t)key0 * D);
+    const bool full = key0 + BN <= Nk;
     if constexpr (!ROWWISE) {
-      const char* kb = (const char*)(K + (size_t)key0 * D);
-      const char* vb = (const char*)(V + (size_t)key0 * D);
-      const bool full = key0 + BN <= Nk;
 #pragma unroll
       for (int m = 0; m < MPW; ++m) {
         const int e = wave + NW * m;  // wave-uniform
         const bool isv = e >= DMA_PER_TILE;
         char* dst = (isv ? vs : ks) + (isv ? e - DMA_PER_TILE : e) * 1024;
-        if (full) {
-          dma16((isv ? vb : kb) + goff[m], dst);
-        } else {
-          const size_t key = (size_t)min(key0 + grow[m], Nk - 1);
-          dma16((isv ? V : K) + key * D + gch[m] * 8, dst);
-        }
+        // a ragged last block re-reads row Nk - 1 for the rows past it
+        const int off = full ? goff[m] : (min(grow[m], Nk - 1 - key0) * ROWB + gch[m] * 16);
+        dma16_buf(isv ? vr : kr, off, dst);
       }
       return;
     }
-    if (key0 + BN <= Nk) {
-      const char* kb = (const char*)(K + (size_t)key0 * D);
-      const char* vb = (const char*)(V + (size_t)key0 * D);
 #pragma unroll
-      for (int i = 0; i < DPW; ++i) {
-        const int blk = wave * DPW + i;
-        dma16(kb + gk[i], ks + blk * 1024);
-        dma16(vb + gv[i], vs + blk * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < DPW; ++i) {
-        const int blk = wave * DPW + i;
+    for (int i = 0; i < DPW; ++i) {
+      const int blk = wave * DPW + i;
+      int ok = gk[i], ov = gv[i];
+      if (!full) {
         const int row = blk * ROWS_PER_DMA + lane / CPR;
         const int pch = lane % CPR;
-        const size_t key = (size_t)min(key0 + row, Nk - 1);
-        dma16(K + key * D + kchunk<D>(row, pch) * 8, ks + blk * 1024);
-        dma16(V + key * D + vchunk<D>(row, pch) * 8, vs + blk * 1024);
+        const int r = min(row, Nk - 1 - key0);
+        ok = r * ROWB + kchunk<D>(row, pch) * 16;
+        ov = r * ROWB + vchunk<D>(row, pch) * 16;
       }
+      dma16_buf(kr, ok, ks + blk * 1024);
+      dma16_buf(vr, ov, vs + blk * 1024);
     }
   };
 
