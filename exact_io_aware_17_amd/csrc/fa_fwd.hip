@@ -422,11 +422,10 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
         const x8 a = __builtin_bit_cast(x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = E::mfma(a, pf[kc], acc[dt]);
       }
-    if constexpr (D == 96 || (D == 128 && BN == 64)) {
+    {
       // Rolling read-ahead: the four transpose reads of the next pair of
       // contraction chunks go out before the two MFMAs of the current pair,
-      // so each pair's LDS latency overlaps the previous pair's matrix work
-      // (+2-3 % at these two instances; no gain or a loss elsewhere).
+      // so each pair's LDS latency overlaps the previous pair's matrix work.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
 #pragma unroll
       for (int g = 0; g < DT * KC / 2; ++g) {
