@@ -88,9 +88,9 @@ constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 
 // Resident workgroups per CU the register budget is sized for: at D = 256 the
 // Q^T fragments and output accumulators alone take 192 registers per lane;
-// 64-key blocks at D = 128 hold two score tiles (210 registers).
+// with 64-key blocks D = 128 needs 202 registers and D = 96 171.
 constexpr int fwd_wg_per_cu(int D, int BN) {
-  return D == 256 ? 1 : (D == 128 && BN == 64 ? 2 : FA_FWD_WG_PER_CU);
+  return D == 256 ? 1 : ((D == 128 || D == 96) && BN == 64 ? 2 : FA_FWD_WG_PER_CU);
 }
 
 // Head dimensions with kernel instances.
@@ -556,19 +556,11 @@ int occupancy() {
   return per;
 }
 
-// Calls f(std::integral_constant<int, BN>) for the block sizes instantiated
-// at head dimension D (64 at D <= 64; 32 and 64 at D = 128; 32 otherwise);
-// returns `fallback` for any other bn.
+// Calls f(std::integral_constant<int, BN>) for the block size instantiated
+// (64 keys at every head dimension); returns `fallback` for any other bn.
 template <int D, typename F, typename R>
 R with_block_keys(int bn, F&& f, R fallback) {
-  if constexpr (D <= 64) {
-    if (bn == 64) return f(std::integral_constant<int, 64>());
-  } else if constexpr (D == 128) {
-    if (bn == 32) return f(std::integral_constant<int, 32>());
-    if (bn == 64) return f(std::integral_constant<int, 64>());
-  } else {
-    if (bn == 32) return f(std::integral_constant<int, 32>());
-  }
+  if (bn == 64) return f(std::integral_constant<int, 64>());
   return fallback;
 }
 

@@ -204,9 +204,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * to max_items of them to `items`, each
  *   tile | part << 16 | (nparts - 1) << 18 | slot_base << 20,
  * in dispatch order; *nslots receives the partial-state slots per head.
- * Query tiles are 128 rows; a tile's keys stream in blocks of 64 keys for
- * d <= 64, of 32 at d = 96 and 256, and at d = 128 of 64 without the causal
- * masks or when Nk >= 4096 and BH * ceil(Nq / 128) <= 4 * cus, else of 32;
+ * Query tiles are 128 rows; a tile's keys stream in blocks of 64 keys;
  * part p of n covers blocks [p * nb / n, (p + 1) * nb / n) of the tile's nb
  * blocks.
  * Returns FA_ERR_INVALID_ARG for invalid arguments.
@@ -216,8 +214,8 @@ int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int o
 
 /*
  * Keys per streamed block that fa_fwd / fa_fwd_ex use for these sizes on the
- * current device (16-bit types; the rule in fa_fwd_schedule's comment with
- * the device's compute units), or FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED.
+ * current device (16-bit types; currently 64 for every supported shape), or
+ * FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED.
  */
 int fa_fwd_block_keys(int B, int H, int Nq, int Nk, int d, int mask_kind);
 

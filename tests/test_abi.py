@@ -210,7 +210,7 @@ def test_block_keys_rule_and_errors():
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 80, 0) == UNS
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 32, 1) == 64
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 64, 1) == 64
-    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 96, 0) == 32
-    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 0) == 64   # no mask: 64 at d = 128
-    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 1) == 32   # short causal rows
-    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 256, 0) == 32
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 96, 0) == 64
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 0) == 64
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 1) == 64
+    assert lib.fa_fwd_block_keys(1, 1, 16, 16, 256, 2) == 64

@@ -23,15 +23,8 @@ BM = 128
 
 
 def block_keys(d, Nq, Nk, BH, causal, cus):
-    """Keys per block of the forward launch (the header's rule)."""
-    if d <= 64:
-        return 64
-    if d != 128:
-        return 32
-    if not causal:
-        return 64
-    tiles = BH * math.ceil(Nq / BM)
-    return 64 if (Nk >= 4096 and cus > 0 and tiles <= 4 * cus) else 32
+    """Keys per block of the forward launch (the header's rule: 64 keys)."""
+    return 64
 ITEM, SPLIT = 2.0, 7.0   # cost per item and extra per split part, in key blocks
 MIN_GAIN = 0.75
 
