@@ -10,11 +10,12 @@
 // Three kernels, no atomics:
 //   prep   D_i and lse_i*log2(e) (+inf for an empty row, so that P = 0) for
 //          every row, into the caller's workspace;
-//   dq     one workgroup per 128 query rows streams the visible key blocks:
-//          S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (the forward's
-//          transposed layout: one query per lane pair);
-//   dkdv   one workgroup per 128 keys streams the query blocks that see
-//          them: S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
+//   dq     one workgroup per 128 query rows streams the visible key blocks
+//          (64 keys, 32 at D = 256): S^T = K Q^T, dP^T = V dO^T, dS^T,
+//          dQ^T += K^T dS^T (the forward's transposed layout: one query per
+//          lane pair);
+//   dkdv   one workgroup per 128 keys streams the blocks of 32 queries that
+//          see them: S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
 //          (one key per lane pair).
 // Streamed blocks go from HBM to LDS with direct 16-byte loads into a double
 // buffer, stored once, row-major. The same copy is read two ways: as rows
@@ -36,7 +37,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int BS = 32;   // streamed rows per block (keys in dq, queries in dkdv)
+constexpr int BS = 32;   // streamed query rows per block in dkdv
 constexpr int NWB = 4;   // waves per workgroup
 constexpr int BT = 32 * NWB;  // rows owned by a workgroup (queries in dq, keys in dkdv)
 
@@ -117,23 +118,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-// DMA of rows [r0, r0 + BS) of two row-major [N, D] 16-bit matrices X0, X1
+// DMA of rows [r0, r0 + ROWS) of two row-major [N, D] 16-bit matrices X0, X1
 // into LDS tiles dst0, dst1 (rows past N repeat row N-1; they are masked by
 // the callers; r0 < N). Each DMA fills 1 KB (64 lanes x 16 bytes) of a tile
 // with a buffer load into LDS from a resource based at row r0 (a 32-bit
 // per-lane offset, no vector address arithmetic; the compiler counts these
 // only in vmcnt, so LDS operand reads are still waited for by count). Where
 // a tile splits into whole rows per DMA and evenly over the waves (D = 64,
-// 128, 256), every wave loads its share of both tiles; otherwise (D = 32,
-// 96) the DMAs of both tiles form one list dealt round-robin over the waves,
+// 128, 256, and D = 32 for 64 rows), every wave loads its share of both
+// tiles; otherwise (D = 96, D = 32 for 32 rows) the DMAs of both tiles form
+// one list dealt round-robin over the waves,
 // lane l of DMA b covering slot 64 b + l of its tile in row-major order.
-template <int D>
+template <int D, int ROWS = BS>
 __device__ __forceinline__ void issue_tiles(const void* __restrict__ X0v,
                                             const void* __restrict__ X1v, int r0, int N,
                                             char* dst0, char* dst1, int wave, int lane) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = ROWB / 16;
-  constexpr int DMA_PER_TILE = BS * ROWB / 1024;
+  constexpr int DMA_PER_TILE = ROWS * ROWB / 1024;
   static_assert((2 * DMA_PER_TILE) % NWB == 0, "the DMAs of two tiles split evenly over the waves");
   const buffer_rsrc b0 = make_rsrc((const char*)X0v + (size_t)r0 * ROWB);
   const buffer_rsrc b1 = make_rsrc((const char*)X1v + (size_t)r0 * ROWB);
@@ -216,11 +218,19 @@ __device__ __forceinline__ void store_rowT(T* dst, const f32x16* acc, float mul,
 }
 
 // ---- dQ: one workgroup per 128 query rows ----
+// Keys stream in blocks of BN (64 at D <= 128, 32 at D = 256, where the
+// registers would not hold two score tiles).
+constexpr int dq_block_keys(int D) { return D <= 128 ? 64 : 32; }
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq_kernel(BwdParams p) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
-  constexpr int TB = BS * D * 2;
+  constexpr int BN = dq_block_keys(D);
+  constexpr int KT = BN / 32;  // 32-key tiles per block
+  constexpr int KC = BN / 16;  // 16-key contraction chunks per block
+  constexpr int ROWB = D * 2;
+  constexpr int TB = BN * ROWB;
   constexpr int DC = D / 16, DT = D / 32;
   // K and V blocks, row-major, one LDS object per stage (so that the
   // compiler sees that the next block's DMA cannot alias this block's reads
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
   int kend = kvlen;
   if (CAUSAL) kend = max(min(kend, q0 + BT + shift), 0);
-  const int nblk = (kend + BS - 1) / BS;
+  const int nblk = (kend + BN - 1) / BN;
 
   const size_t head = (size_t)bh * N * D;
   const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
@@ -279,75 +289,79 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   auto issue = [&](int j, auto stage) {
     constexpr int SD = decltype(stage)::value;
     if (j >= nblk) return;
-    issue_tiles<D>(K, V, j * BS, Nk, SD == 0 ? kbuf0 : kbuf1, SD == 0 ? vbuf0 : vbuf1, wave, lane);
+    issue_tiles<D, BN>(K, V, j * BN, Nk, SD == 0 ? kbuf0 : kbuf1, SD == 0 ? vbuf0 : vbuf1, wave,
+                       lane);
   };
   auto step = [&](int j, auto stage) {
     constexpr int ST = decltype(stage)::value;
     wait_vmem();
     __syncthreads();
     issue(j + 1, std::integral_constant<int, 1 - ST>());
-    const int key0 = j * BS;
+    const int key0 = j * BN;
     if (CAUSAL && key0 > qa + 31 + shift) return;  // wholly in this wave's future
     const char* ks = ST == 0 ? kbuf0 : kbuf1;
     const char* vs = ST == 0 ? vbuf0 : vbuf1;
 
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s, dp;
-    zero(s);
-    zero(dp);
-    if constexpr (D <= 128) {
-      // All K operand reads first, then the S^T products with the V operand
-      // reads in between, then dP^T: one LDS latency ahead of the matrix
-      // work instead of one per pair of reads (the scheduler alone keeps two
-      // reads in flight). At D = 256 the operands would not fit the registers.
-      x8 kop[DC], vop[DC];
+    f32x16 s[KT], dp[KT];
 #pragma unroll
-      for (int c = 0; c < DC; ++c) kop[c] = *(const x8*)(ks + off.roff[c]);
+    for (int t = 0; t < KT; ++t) {
+      zero(s[t]);
+      zero(dp[t]);
+    }
+    if constexpr (KT == 2) {
+      // Two key tiles: the operands of both would not fit the registers, so
+      // the reads roll one chunk ahead over the 2 * DC chunks (K, then V):
+      // the reads of chunk c+1 go out before the MFMAs of chunk c.
 #pragma unroll
-      for (int c = 0; c < DC; ++c) vop[c] = *(const x8*)(vs + off.roff[c]);
+      for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int c = 0; c < DC; ++c) s = E::mfma(kop[c], qf[c], s);
+        for (int t = 0; t < KT; ++t) s[t] = E::mfma(*(const x8*)(ks + t * 32 * ROWB + off.roff[c]), qf[c], s[t]);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) dp = E::mfma(vop[c], of[c], dp);
-      __builtin_amdgcn_sched_group_barrier(0x100, DC, 0);  // DS reads (K)
+      for (int c = 0; c < DC; ++c)
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA (S^T)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read (V)
+        for (int t = 0; t < KT; ++t) dp[t] = E::mfma(*(const x8*)(vs + t * 32 * ROWB + off.roff[c]), of[c], dp[t]);
+      __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+#pragma unroll
+      for (int c = 0; c < 2 * DC; ++c) {
+        if (c + 1 < 2 * DC) __builtin_amdgcn_sched_group_barrier(0x100, KT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KT, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, DC, 0);  // MFMAs (dP^T)
     } else {
+      // One tile at D = 256, where the operands would not fit the registers.
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        s = E::mfma(*(const x8*)(ks + off.roff[c]), qf[c], s);
-        dp = E::mfma(*(const x8*)(vs + off.roff[c]), of[c], dp);
+        s[0] = E::mfma(*(const x8*)(ks + off.roff[c]), qf[c], s[0]);
+        dp[0] = E::mfma(*(const x8*)(vs + off.roff[c]), of[c], dp[0]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
     // Hidden keys (only in blocks that straddle the diagonal or kv_len): the
     // score becomes -inf, so its P is exactly 0. A uniform branch of its own,
     // so unmasked blocks pay nothing for it.
-    const bool need_mask = (key0 + BS > kvlen) || (CAUSAL && key0 + BS - 1 > qa + shift);
+    const bool need_mask = (key0 + BN > kvlen) || (CAUSAL && key0 + BN - 1 > qa + shift);
     if (need_mask) {
       int lim = kvlen - 1;  // key visible iff key <= lim
       if (CAUSAL) lim = min(lim, qrow + shift);
       lim -= key0 + 4 * h;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) > lim) s[r] = NEG_INF;
-    }
-    x8 df[2];
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+        for (int r = 0; r < 16; ++r)
+          if (t * 32 + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = NEG_INF;
+    }
+    x8 df[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float v2[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int r = 8 * kc + 2 * e + u;
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -lse2));
-          v2[u] = pv * (dp[r] - dl);  // dS^T
+          const int r = 8 * (kc & 1) + 2 * e + u;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], scl, -lse2));
+          v2[u] = pv * (dp[kc >> 1][r] - dl);  // dS^T
         }
         w[e] = E::pack(v2[0], v2[1]);
       }
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) acc[dt] = E::mfma(tr_operand<x8, D>(ks, off, dt, kc), df[kc], acc[dt]);
+      for (int kc = 0; kc < KC; ++kc) acc[dt] = E::mfma(tr_operand<x8, D>(ks, off, dt, kc), df[kc], acc[dt]);
     __builtin_amdgcn_s_setprio(0);
   };
   issue(0, std::integral_constant<int, 0>());
