@@ -17,14 +17,22 @@ kernels are launched on (torch's current stream, which the binding passes to
 libfa). The roofline's kernel duration is the average launch duration over
 the timed region (its two events divided by the K launches it holds); an
 event pair around each of K further launches is reported beside it
-("per_launch_events").
+("per_launch_events", mean, median and min), and so is a third set of K
+launches each preceded by a 512 MiB write that evicts the L2 and the
+Infinity Cache ("per_launch_flushed": Q, K and V then come from HBM). The
+matrix-core ceiling of the device at hand is measured too ("mfma_probe":
+libfa_probe's bf16 MFMA-only kernel, launches of the forward's FLOPs timed
+the same two ways), so that the forward's rate can be read against the
+published peak and against what the matrix cores sustain here.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +43,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2h16n4096d128_traffic.json")
+PROBE_LIB = os.path.join(ROOT, "exact_io_aware_17_amd", "libfa_probe.so")
+FLUSH_BYTES = 512 * 2 ** 20  # > 8 x 4 MB of L2 + 256 MB of Infinity Cache
 SWEEP_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_bh32d128_traffic_sweep.json")
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)  # causal, B=2, H=16, d=128
 KERNEL_SOURCES = [
@@ -267,6 +277,65 @@ def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
     return res
 
 
+def timing_summary(ms, flops):
+    """mean / median / min of per-launch times (ms) and the mean's TFLOP/s."""
+    mean = sum(ms) / len(ms)
+    return {"ms_mean": round(mean, 5), "ms_median": round(statistics.median(ms), 5),
+            "ms_min": round(min(ms), 5), "tflops_mean": round(flops / (mean * 1e-3) / 1e12, 2)}
+
+
+def mfma_probe(dev, stream, flops_target, reps, warmup=3):
+    """The matrix-core rate this device sustains: libfa_probe's kernel (bf16
+    32x32x16 MFMAs only, two 256-thread workgroups per CU), each launch sized
+    to about flops_target, timed back to back and with an event pair around
+    each launch."""
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it with "
+                           "python -m exact_io_aware_17_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fa_probe_mfma_bf16.restype = ctypes.c_int
+    lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.fa_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = max(1, round(flops_target / lib.fa_probe_mfma_bf16_flops(wgs, 1)))
+    flops = lib.fa_probe_mfma_bf16_flops(wgs, iters)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def once():
+        r = lib.fa_probe_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"fa_probe_mfma_bf16 returned {r}")
+
+    for _ in range(warmup):
+        once()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        once()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_b2b = a.elapsed_time(b) / reps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        once()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = timing_summary([a.elapsed_time(b) for a, b in evs], flops)
+    return {"what": "bf16 v_mfma_f32_32x32x16 only: 4 independent chains per wave, "
+                    "2 workgroups of 4 waves per CU, launches of the forward's FLOPs",
+            "workgroups": wgs, "iters": iters, "flops_per_launch": flops,
+            "back_to_back": {"ms_mean": round(ms_b2b, 5),
+                             "tflops_mean": round(flops / (ms_b2b * 1e-3) / 1e12, 2)},
+            "per_launch_events": per}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +347,8 @@ def main() -> int:
     ap.add_argument("--no-split-kv", action="store_true",
                     help="skip the split-KV comparison (it launches the forward kernel "
                          "at another shape)")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the matrix-core rate probe")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run (copy calibration + forward) for rocprofv3 counters")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -336,8 +407,19 @@ def main() -> int:
         fwd_once()
         b.record(stream)
     torch.cuda.synchronize()
-    per_launch = sorted(a.elapsed_time(b) for a, b in evs)
-    ms_kernel = sum(per_launch) / len(per_launch)
+    per_launch = [a.elapsed_time(b) for a, b in evs]
+
+    # The same with L2 and the Infinity Cache flushed before each launch (a
+    # fill kernel over 512 MiB between the launches, outside the event pair).
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for a, b in evs:
+        flush.zero_()
+        a.record(stream)
+        fwd_once()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_launch_flushed = [a.elapsed_time(b) for a, b in evs]
+    del flush
 
     flops = W.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -375,12 +457,12 @@ def main() -> int:
             "kernel_ms_mean": round(ms_step, 5),
             "algorithmic_hbm_bytes": W.fwd_bytes(w.B, w.H, w.N, w.d, 2),
         },
-        "per_launch_events": {
-            "what": "event pair around each of K launches after the timed region",
-            "ms_mean": round(ms_kernel, 5),
-            "ms_min": round(per_launch[0], 5),
-            "tflops_mean": round(flops / (ms_kernel * 1e-3) / 1e12, 2),
-        },
+        "per_launch_events": dict(
+            {"what": "event pair around each of K launches after the timed region"},
+            **timing_summary(per_launch, flops)),
+        "per_launch_flushed": dict(
+            {"what": "the same, a 512 MiB fill (L2 and Infinity Cache evicted) before each launch"},
+            **timing_summary(per_launch_flushed, flops)),
     }
 
     if not args.no_bwd:
@@ -418,6 +500,14 @@ def main() -> int:
             out["split_kv"] = split_kv_comparison(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
+
+    if not args.no_mfma_probe:
+        pr = mfma_probe(dev, stream, flops, args.steps)
+        pr["fwd_over_probe_back_to_back"] = round(
+            tflops / pr["back_to_back"]["tflops_mean"], 4)
+        pr["fwd_over_probe_per_launch"] = round(
+            out["per_launch_events"]["tflops_mean"] / pr["per_launch_events"]["tflops_mean"], 4)
+        out["mfma_probe"] = pr
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, w)

@@ -3,9 +3,11 @@
     python -m exact_io_aware_17_amd.build
 
 Compiles every source under csrc/ with hipcc for --offload-arch=gfx950 into
-exact_io_aware_17_amd/_build/, then links exact_io_aware_17_amd/libfa.so.
-Always recompiles (it is also the "does it build" check on machines without a
-GPU, where hipcc cross-compiles).
+exact_io_aware_17_amd/_build/, then links exact_io_aware_17_amd/libfa.so, and
+links the matrix-core rate probe (csrc/probe/) into libfa_probe.so, a
+separate library that only the benchmark loads. Always recompiles (it is also
+the "does it build" check on machines without a GPU, where hipcc
+cross-compiles).
 """
 from __future__ import annotations
 
@@ -20,8 +22,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
+PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
 
 SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
+PROBE_SOURCES = ["probe/fa_probe.hip"]
 
 # Per-source extra flags. The 16-bit forward keeps its MFMA accumulators in
 # VGPRs (its rare rescale multiplies them with VALU instructions, which cannot
@@ -50,7 +54,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = ([hipcc()] + COMMON + EXTRA.get(src, []) + list(extra)
            + ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,19 +63,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile all sources and link libfa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile all sources, link libfa.so and libfa_probe.so; returns the
+    path of libfa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
