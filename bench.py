@@ -78,7 +78,10 @@ def measured_traffic():
 
 def cpu_baseline(x, w, budget_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample: whole heads of the
-    same workload, one after another, until the time budget is used."""
+    same workload, one after another, until the time budget is used. With
+    per-batch key lengths the sample starts with one seeded head of every
+    batch (so every length is in it) and the line also reports the seconds
+    per head and, labelled as such, their extrapolation to every head."""
     import numpy as np
     from oracle import attention as orc
     from exact_io_aware_17_amd import workloads as W
@@ -94,6 +97,10 @@ def cpu_baseline(x, w, budget_s: float = 12.0):
     v = x["v"].double().numpy()
     kv = None if "kv_lens" not in x else [int(a) for a in x["kv_lens"].tolist()]
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if kv is not None:
+        rng = np.random.default_rng(w.seed)
+        first = [(b, int(rng.integers(0, w.H))) for b in range(w.B)]
+        heads = first + [bh for bh in heads if bh not in first]
     done = 0
     t0 = time.perf_counter()
     for bh in heads:
@@ -103,14 +110,23 @@ def cpu_baseline(x, w, budget_s: float = 12.0):
             break
     dt = time.perf_counter() - t0
     flops = W.fwd_flops(1, done, w.N, w.d, w.causal)
-    return {
+    out = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads (full N={w.N} rows each), fp64 numpy, "
                   f"{dt:.1f} s",
+        "s_per_head": round(dt / done, 3),
     }
+    if done < len(heads):
+        out["extrapolated_all_heads_s"] = round(dt / done * len(heads), 1)
+    if kv is not None:
+        out["note"] = ("FLOPs counted as the nominal 4*N^2*d (/2 causal) per head: the oracle "
+                       "forms every score and hides the keys past kv_len; heads of batches "
+                       + ", ".join(f"{b} (kv_len {kv[b]})" for b, _ in heads[:min(done, w.B)])
+                       + " in the sample")
+    return out
 
 
 COPY_BYTES = 256 * 2 ** 20  # calibration copy: 256 MiB read + 256 MiB written
@@ -348,6 +364,8 @@ def main() -> int:
     ap.add_argument("--no-split-kv", action="store_true",
                     help="skip the split-KV comparison (it launches the forward kernel "
                          "at another shape)")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time only the fp64 oracle on the workload (no GPU needed)")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the matrix-core rate probe")
     ap.add_argument("--profile-run", action="store_true",
@@ -373,6 +391,10 @@ def main() -> int:
     w = W.BY_ID[args.workload]
     if args.profile_run:
         return profile_run(w)
+    if args.cpu_baseline_only:
+        print(json.dumps({"workload": w.name, "cpu_baseline": cpu_baseline(W.make_inputs(w), w),
+                          "cpus": os.cpu_count()}), flush=True)
+        return 0
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = W.make_inputs(W.with_shape(w, backward=True))

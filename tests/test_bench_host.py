@@ -98,3 +98,14 @@ def test_measured_traffic_only_for_the_current_kernel_sources(tmp_path, monkeypa
     assert bench.measured_traffic() is None
     p.unlink()
     assert bench.measured_traffic() is None
+
+
+def test_cpu_baseline_only_times_the_oracle_without_a_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "1",
+                        "--cpu-baseline-only"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    cb = line["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert cb["sample"].startswith("1 of 1 heads")
+    assert "extrapolated_all_heads_s" not in cb  # the whole workload was timed
