@@ -246,19 +246,25 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
       }
       return;
     }
+    // One uniform branch per block: a full block issues its DMAs with the
+    // precomputed offsets, straight through.
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int blk = wave * DPW + i;
+        dma16_buf(kr, gk[i], ks + blk * 1024);
+        dma16_buf(vr, gv[i], vs + blk * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int blk = wave * DPW + i;
-      int ok = gk[i], ov = gv[i];
-      if (!full) {
-        const int row = blk * ROWS_PER_DMA + lane / CPR;
-        const int pch = lane % CPR;
-        const int r = min(row, Nk - 1 - key0);
-        ok = r * ROWB + kchunk<D>(row, pch) * 16;
-        ov = r * ROWB + vchunk<D>(row, pch) * 16;
-      }
-      dma16_buf(kr, ok, ks + blk * 1024);
-      dma16_buf(vr, ov, vs + blk * 1024);
+      const int row = blk * ROWS_PER_DMA + lane / CPR;
+      const int pch = lane % CPR;
+      const int r = min(row, Nk - 1 - key0);
+      dma16_buf(kr, r * ROWB + kchunk<D>(row, pch) * 16, ks + blk * 1024);
+      dma16_buf(vr, r * ROWB + vchunk<D>(row, pch) * 16, vs + blk * 1024);
     }
   };
 
