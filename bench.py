@@ -474,7 +474,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, 2, "
+            "kernel": f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, "
                       f"{'true' if w.causal else 'false'}>",
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_step, 5),

@@ -76,9 +76,6 @@ static_assert(BM == FWD_BM, "workgroup tile matches the host planner");
 constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
 constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
 
-#ifndef FA_FWD_STAGES
-#define FA_FWD_STAGES 2
-#endif
 #ifndef FA_PRIO_MFMA
 #define FA_PRIO_MFMA 1  // wave priority (s_setprio) during the MFMA phases
 #endif
@@ -96,7 +93,7 @@ constexpr int fwd_wg_per_cu(int D, int BN) {
 // Head dimensions with kernel instances.
 #define FA_FOR_EACH_D(X) X(32) X(64) X(96) X(128) X(256)
 
-template <typename T, int D, int BN, int STAGES, bool CAUSAL>
+template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdParams p, FwdPlan plan) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
@@ -118,7 +115,6 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
   constexpr int KC = BN / 16;                 // 16-key contraction chunks per block
   static_assert((2 * DMA_PER_TILE) % NW == 0, "the DMAs of a block split evenly over the waves");
   static_assert(BN == 32 || BN == 64, "block of 32 or 64 keys");
-  static_assert(STAGES == 2, "double-buffered K/V stream");
 
   // One LDS object per stage and operand: the compiler then knows that the
   // DMA into one stage cannot alias the reads of the other, and the block's
@@ -538,16 +534,15 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
 
 template <typename T, int D, int BN>
 hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
-  constexpr int ST = FA_FWD_STAGES;
   const long long ntiles = (p.N + BM - 1) / BM;
   const long long items = plan.nitems > 0 ? plan.nitems : ntiles;
   const long long grid = (long long)p.B * p.H * items;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BN, ST, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
                        stream, p, plan);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BN, ST, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
                        stream, p, plan);
   return hipGetLastError();
 }
@@ -556,7 +551,7 @@ template <typename T, int D, int BN, bool CAUSAL>
 int occupancy() {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, BN, FA_FWD_STAGES, CAUSAL>), NW * 64,
+          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, BN, CAUSAL>), NW * 64,
           0) != hipSuccess)
     return 0;
   return per;

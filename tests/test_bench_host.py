@@ -36,7 +36,7 @@ def _write_counter_csv(path, counter, rows):
 def _profile_dispatches(copy_kib, fwd_kib, sweep_kib, naive_kib):
     # the dispatch order of --profile-run: a fill, three copies, three
     # workload forwards, one forward per sweep N, then the naive kernels
-    fwd = "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELi64ELi2ELb1EEEvNS_9FwdParamsENS_7FwdPlanE"
+    fwd = "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELi64ELb1EEEvNS_9FwdParamsENS_7FwdPlanE"
     rows = [("fill_kernel", 1.0)]
     rows += [("copy_kernel", copy_kib)] * 3
     rows += [(fwd, v) for v in fwd_kib]
