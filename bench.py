@@ -53,6 +53,7 @@ KERNEL_SOURCES = [
     for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")
 ]
 FWD_KERNEL_TAG = "fwd_kernel"  # in the forward kernel's name, mangled or not
+BWD_KERNEL_TAG = "bwd_"        # in the backward kernels' names (prep, dK/dV, dQ)
 
 
 def kernel_source_hash() -> str:
@@ -136,7 +137,7 @@ def profile_run(w) -> int:
     """A short run for counter collection: a plain copy of known size three
     times, the forward kernel on the workload three times, then once at each
     N of the traffic sweep (causal, B=2, H=16, d=128), then the naive
-    forward once on the workload."""
+    forward once on the workload, then one fa_bwd on the workload."""
     import torch
     import exact_io_aware_17_amd as fa
     from exact_io_aware_17_amd import workloads as W
@@ -152,7 +153,7 @@ def profile_run(w) -> int:
         dst.copy_(src)
     torch.cuda.synchronize()
     for _ in range(3):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kv)
+        o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kv)
     torch.cuda.synchronize()
     print("profile run: workload done", flush=True)
     for n in SWEEP_N:
@@ -166,6 +167,10 @@ def profile_run(w) -> int:
     naive_forward(q, k, v, w.scale, w.causal)
     torch.cuda.synchronize()
     print("profile run: naive forward done", flush=True)
+    do = W.make_inputs(W.with_shape(w, backward=True))["do"].to(dev)
+    fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, kv_lens=kv)
+    torch.cuda.synchronize()
+    print("profile run: backward done", flush=True)
     return 0
 
 
@@ -205,8 +210,10 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
             return 1
         scale = COPY_BYTES / (sorted(copy)[len(copy) // 2] * 1024.0)
         last_fwd = max(i for i, n, _ in rows if FWD_KERNEL_TAG in n)
-        naive = sum(v for i, _, v in rows if i > last_fwd) * 1024.0 * scale
+        naive = sum(v for i, n, v in rows if i > last_fwd and BWD_KERNEL_TAG not in n) * 1024.0 * scale
         out["naive_" + key + "_bytes"] = naive
+        # one fa_bwd call (prep + dK/dV + dQ) on the workload, after the naive forward
+        out["bwd_" + key + "_bytes"] = sum(v for _, n, v in rows if BWD_KERNEL_TAG in n) * 1024.0 * scale
         wl = sorted(fwd[:3])[1]
         out[key + "_kib_raw"] = wl
         out[key + "_scale"] = scale
