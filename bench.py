@@ -41,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector (the fp32 forward uses FMAs, not MFMA)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_b2h16n4096d128_traffic.json")
 TRAFFIC_WORKLOAD = 5  # the workload (causal B=2 H=16 N=4096 d=128) TRAFFIC_FILE was measured on
@@ -457,6 +458,8 @@ def main() -> int:
     # duration is ms_step.
     achieved = tflops
     traffic = measured_traffic() if args.workload == TRAFFIC_WORKLOAD else None
+    f32 = w.dtype == "f32"
+    peak = PEAK_F32_VECTOR_TFLOPS if f32 else PEAK_BF16_TFLOPS
 
     out = {
         "metric": "attention fwd TFLOP/s & % bf16 MFMA peak (causal, N=4096, d=128) on 1 MI355X",
@@ -469,20 +472,21 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "bound": "mfma",
+            "bound": "alu" if f32 else "mfma",
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, "
-                      f"{'true' if w.causal else 'false'}>",
+            "kernel": (f"fwd_f32_kernel<{w.d}, {'true' if w.causal else 'false'}>" if f32 else
+                       f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, "
+                       f"{'true' if w.causal else 'false'}>"),
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_step, 5),
             "algorithmic_hbm_bytes": W.fwd_bytes(w.B, w.H, w.N, w.d, 2),
