@@ -8,9 +8,11 @@ memory when timing starts. A timed step is one fa_fwd launch over the whole
 batch (value = forward TFLOP/s at 4*B*H*N^2*d/2 FLOPs). The backward pass is
 timed the same way and reported beside it ("bwd"), together with one full
 forward+backward pass ("fwd_bwd_step"), fa_fwd_ex (split-KV) is compared with
-fa_fwd on a grid too small to fill the GPU ("split_kv"), and a naive forward
-that materialises S and P in device memory (PyTorch matmul + softmax, the
-comparison path, not part of libfa) is timed on the same inputs ("naive").
+fa_fwd on a grid too small to fill the GPU ("split_kv") and on decode, one
+query row per head over a long cache, against the HBM peak ("decode"), and a
+naive forward that materialises S and P in device memory (PyTorch matmul +
+softmax, the comparison path, not part of libfa) is timed on the same inputs
+("naive").
 
 Prints ONE JSON line. Timing uses HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
@@ -361,6 +363,38 @@ def mfma_probe(dev, stream, flops_target, reps, warmup=3):
             "per_launch_events": per}
 
 
+def decode_comparison(dev, stream, B=8, H=32, Hkv=8, Nk=32768, d=128, reps=20):
+    """Decode: one query row per head over a long K/V cache with grouped heads
+    (causal, so the query sees every key). Bound by HBM, not the matrix
+    cores: the rate is the bytes of Q, K, V, O and lse per second against
+    the 8 TB/s peak. fa_fwd_ex without and with the split-KV plan (a single
+    query tile per head is one workgroup unless its key range is split)."""
+    import torch
+    import exact_io_aware_17_amd as fa
+
+    g = torch.Generator().manual_seed(17098)
+    q = torch.randn(B, H, 1, d, generator=g).to(torch.bfloat16).to(dev)
+    k, v = (torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16).to(dev) for _ in range(2))
+    nbytes = 2 * q.numel() * 2 + (k.numel() + v.numel()) * 2 + B * H * 4
+    res = {"shape": f"causal B={B} H={H} Hkv={Hkv} Nq=1 Nk={Nk} d={d}", "bytes": nbytes}
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    for name, split in (("fa_fwd_ex", False), ("fa_fwd_ex_split", True)):
+        for _ in range(3):
+            fa.fwd(q, k, v, causal=True, split=split)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fa.fwd(q, k, v, causal=True, split=split)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 5), "gb_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -532,6 +566,7 @@ def main() -> int:
     if not args.no_bwd:
         if not args.no_split_kv:
             out["split_kv"] = split_kv_comparison(dev, stream)
+            out["decode"] = decode_comparison(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
 

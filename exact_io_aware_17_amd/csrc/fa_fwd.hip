@@ -299,9 +299,11 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     wait_vmem();
     __syncthreads();
     const int key0 = j * BN;
-    // Blocks wholly in this wave's future (all its rows would be masked) are
-    // skipped; the wave still issues its share of the next block's DMA.
-    const bool skip = CAUSAL && key0 > qa + 31 + shift;
+    // Blocks wholly in this wave's future (all its rows would be masked), and
+    // every block of a wave whose rows all lie past the last query (decode,
+    // a ragged last tile), are skipped; the wave still issues its share of
+    // the next block's DMA.
+    const bool skip = (CAUSAL && key0 > qa + 31 + shift) || qa >= N;
     const char* ks = ST == 0 ? kbuf0 : kbuf1;
     const char* vs = ST == 0 ? vbuf0 : vbuf1;
 
