@@ -35,6 +35,22 @@ int check_common(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int 
   return FA_OK;
 }
 
+// Decode with grouped K/V heads: with one query row per head the G = H / Hkv
+// query heads that share a K/V head are G adjacent rows of q and o (a
+// [B, H, 1, d] tensor is laid out as [B, Hkv, G, d]) and of lse, and that
+// one query sees every key under the non-strict causal mask (it sits at the
+// last key's position). Launched as Hkv heads of G query rows without the
+// mask, each K/V head is streamed once instead of once per query head; the
+// rows, their keys and their results are the same. Rewrites the launch
+// shape in place (16-bit paths only; the strict mask hides the last key, so
+// it keeps the per-head launch).
+void pack_decode(int& H, int Hkv, int& Nq, int& mask_kind) {
+  if (Nq != 1 || H == Hkv || mask_kind == FA_MASK_CAUSAL_STRICT) return;
+  Nq = H / Hkv;
+  H = Hkv;
+  mask_kind = FA_MASK_NONE;
+}
+
 bool valid_dtype(int dtype) {
   return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16 || dtype == FA_DTYPE_F32;
 }
@@ -110,6 +126,10 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     hipError_t e = fa::launch_fwd_f32(p, (hipStream_t)stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
+  pack_decode(H, Hkv, Nq, mask_kind);
+  p.H = H;
+  p.N = Nq;
+  p.causal = (mask_kind != FA_MASK_NONE);
   const int BH = B * H;
   const int cus = fa::fwd_device_cus();
   p.bn = fa::fwd_block_keys(d, Nq, Nk, BH, p.causal != 0, cus);
@@ -218,6 +238,7 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
                                  int mask_kind) {
   if (check_common(B, H, Hkv, Nq, Nk, d, 1.f, mask_kind) != FA_OK) return 0;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return 0;  // fp32: never split
+  pack_decode(H, Hkv, Nq, mask_kind);  // the launch shape fa_fwd_ex plans for
   const bool causal = (mask_kind != FA_MASK_NONE);
   const int cus = fa::fwd_device_cus();
   const int bn = fa::fwd_block_keys(d, Nq, Nk, B * H, causal, cus);

@@ -28,6 +28,9 @@ CASES = [
     (2, 4, 4, 200, 700, 128, True, None),      # continuation after 500 cached keys
     (2, 4, 2, 700, 200, 64, True, None),       # first 500 queries see no key
     (1, 4, 2, 1, 4096, 128, True, None),       # decode: one query per head
+    (2, 32, 4, 1, 5000, 64, False, [4000, 1]),  # decode, 8 heads per K/V head, padded keys
+    (1, 8, 2, 1, 3000, 128, "strict", None),   # strict decode (hides the last key)
+    (1, 256, 1, 1, 700, 128, True, [700]),     # one K/V head for 256 query heads (two tiles)
     (2, 8, 2, 16, 2000, 128, False, [1500, 0]),  # short queries, padded keys, an empty batch
     (1, 4, 4, 130, 1000, 64, "strict", None),
     (1, 2, 1, 1000, 33, 128, "strict", [20]),  # Nq > Nk with padding
