@@ -140,6 +140,11 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
  *               Not used with FA_DTYPE_F32.
  * With FA_DTYPE_F16 the probabilities are rounded to fp16 (not bf16) before
  * the P V product and O is written in fp16 (round-to-nearest-even).
+ * Decode with grouped heads (Nq = 1, H > Hkv, no mask or the causal one;
+ * 16-bit types): the H / Hkv query heads of a K/V head are launched as rows
+ * of one query tile, so each K/V head is streamed once; the results are
+ * those of the per-head launch up to the rounding of a different key split,
+ * and fa_fwd_ex_workspace_bytes sizes the workspace for this launch.
  * Errors as fa_fwd, and FA_ERR_INVALID_ARG for an unknown dtype or for
  * workspace_bytes > 0 with a NULL workspace, FA_ERR_UNSUPPORTED for a
  * workspace not 16-byte aligned.
