@@ -48,7 +48,7 @@
 //    straddle the diagonal or the padding length apply a mask.
 //  * A row with no visible key keeps l = 0 and is written as O = 0 and
 //    lse = -inf ("Worked examples", Cell D2).
-//  * Load balance: a host plan may cut a tile's key range into up to four
+//  * Load balance: a host plan may cut a tile's key range into up to 16
 //    parts processed by different workgroups. Each part stores its partial
 //    state (unnormalised O, reference max, both sums; fp32) and counts its
 //    arrival on the tile's counter; the last part to arrive merges all parts
@@ -145,9 +145,9 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
   int tile, part = 0, nparts = 1, slot_base = 0;
   if (plan.nitems > 0) {
     const unsigned it = plan.item[rank];
-    tile = (int)(it & 0xffffu);
-    part = (int)((it >> 16) & 3u);
-    nparts = (int)((it >> 18) & 3u) + 1;
+    tile = (int)(it & 0xfffu);
+    part = (int)((it >> 12) & 15u);
+    nparts = (int)((it >> 16) & 15u) + 1;
     slot_base = (int)(it >> 20);
   } else {
     tile = CAUSAL ? ntiles - 1 - rank : rank;  // causal: the latest rows see the most keys
@@ -484,20 +484,19 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
 
     // Every part, this one included, is read back and combined in part
     // order: the result does not depend on which part arrived last.
-    f32x4 stat[4];
+    // The row statistics are read twice (max first, then the sums), so any
+    // number of parts merges in the same registers.
     float m_all = NEG_INF;
-    for (int q = 0; q < nparts; ++q) {
-      stat[q] = load_coherent16(rm, q * SLOT_ML + vm);
-      m_all = fmaxf(m_all, stat[q][0]);
-    }
+    for (int q = 0; q < nparts; ++q) m_all = fmaxf(m_all, load_coherent16(rm, q * SLOT_ML + vm)[0]);
     float l_sum = 0.f, lbf_sum = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
     for (int q = 0; q < nparts; ++q) {
-      const float m_q = stat[q][0];
+      const f32x4 stat = load_coherent16(rm, q * SLOT_ML + vm);
+      const float m_q = stat[0];
       const float c = (m_q == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_q - m_all);
-      l_sum = fmaf(c, stat[q][1], l_sum);
-      lbf_sum = fmaf(c, stat[q][2], lbf_sum);
+      l_sum = fmaf(c, stat[1], l_sum);
+      lbf_sum = fmaf(c, stat[2], lbf_sum);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll

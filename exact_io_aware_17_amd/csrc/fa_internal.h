@@ -45,13 +45,15 @@ int fwd_block_keys(int d, int Nq, int Nk, int BH, bool causal, int cus);
 int fwd_device_cus();
 constexpr int FWD_ML_FLOATS = 4 * 2 * FWD_BM;  // {m, l, l_bf, 0} for each of 2*BM lanes
 constexpr int FWD_PLAN_MAX = 512;
+constexpr int FWD_MAX_PARTS = 16;  // key-range parts of one split tile
 // Arrival counters occupy a fixed region at the start of every forward
 // workspace, whatever the shape, so a workspace reused for another shape
 // still finds them zero: plans are made only when B*H*ntiles fits.
 constexpr int FWD_COUNTERS = 16384;
 
 // Work items of the forward, in dispatch order (the same list for every
-// (b, h)). Item: tile | part << 16 | (nparts - 1) << 18 | slot_base << 20.
+// (b, h)). Item: tile | part << 12 | (nparts - 1) << 16 | slot_base << 20
+// (tile < 4096, nparts <= FWD_MAX_PARTS, slot_base < 4096).
 // Part `part` of `nparts` covers key blocks [part*nb/nparts, (part+1)*nb/nparts)
 // of the tile's nb nominal blocks; split parts use partial-state slots
 // slot_base + part.

@@ -6,7 +6,7 @@
 // causal mask the tiles of late query rows stream up to N/BN blocks and early
 // ones a few, and without it N/BM tiles of equal cost may fill the resident
 // slots unevenly; either way the last workgroups can leave most of the chip
-// idle. The planner splits the heaviest tiles into up to four contiguous key
+// idle. The planner splits the heaviest tiles into up to sixteen contiguous key
 // ranges (the block merge of the online softmax, "Exercises" of the
 // interactive explainer "The Flash Attention", combines their partial states
 // exactly), orders all items longest first, and keeps the split threshold
@@ -143,7 +143,7 @@ std::vector<Item> make_items(int N, int Nk, bool causal, int bn, int T) {
   for (int t = 0; t < ntiles; ++t) {
     const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
     int np = 1;
-    if (T > 0 && nb > T) np = std::min(4, (nb + T - 1) / T);
+    if (T > 0 && nb > T) np = std::min(FWD_MAX_PARTS, (nb + T - 1) / T);
     for (int part = 0; part < np; ++part) {
       const int blocks = (part + 1) * nb / np - part * nb / np;
       items.push_back({t, part, np, blocks + kItemCost + (np > 1 ? kSplitCost : 0.0)});
@@ -163,14 +163,14 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
   plan->nslots = 0;
   const int ntiles = (N + FWD_BM - 1) / FWD_BM;
   const long long slots = (long long)cus * occ;
-  if (cus <= 0 || occ <= 0 || ntiles > 0xffff || (long long)BH * ntiles >= kMaxWaves * slots ||
+  if (cus <= 0 || occ <= 0 || ntiles > 0xfff || (long long)BH * ntiles >= kMaxWaves * slots ||
       (long long)BH * ntiles > FWD_COUNTERS)
     return plan;
   const int nbmax = fwd_tile_blocks(N, Nk, ntiles - 1, causal, bn);
   const double base = simulate(make_items(N, Nk, causal, bn, 0), BH, cus, occ);
   double best = base * kMinGain;
   int bestT = 0;
-  static const double fracs[] = {0.875, 0.75, 0.625, 0.5, 0.4, 1.0 / 3.0, 0.25};
+  static const double fracs[] = {0.875, 0.75, 0.625, 0.5, 0.4, 1.0 / 3.0, 0.25, 0.125, 0.0625};
   for (double f : fracs) {
     const int T = std::max(4, (int)(nbmax * f + 0.999));
     if (T >= nbmax) continue;
@@ -189,7 +189,7 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
   int nslots = 0;
   for (int t = 0; t < ntiles; ++t) {
     const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
-    const int np = (nb > bestT) ? std::min(4, (nb + bestT - 1) / bestT) : 1;
+    const int np = (nb > bestT) ? std::min(FWD_MAX_PARTS, (nb + bestT - 1) / bestT) : 1;
     base_of[t] = nslots;
     if (np > 1) nslots += np;
   }
@@ -197,7 +197,7 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
   for (size_t i = 0; i < items.size(); ++i) {
     const Item& it = items[i];
     const int sb = (it.nparts > 1) ? base_of[it.tile] : 0;
-    plan->item[i] = (uint32_t)it.tile | ((uint32_t)it.part << 16) | ((uint32_t)(it.nparts - 1) << 18) |
+    plan->item[i] = (uint32_t)it.tile | ((uint32_t)it.part << 12) | ((uint32_t)(it.nparts - 1) << 16) |
                     ((uint32_t)sb << 20);
   }
   plan->nitems = (int)items.size();

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_OK = 0,
@@ -207,7 +207,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * compute units and `occ` resident workgroups per compute unit, returns the
  * number of work items (0 = one item per query tile, no split) and copies up
  * to max_items of them to `items`, each
- *   tile | part << 16 | (nparts - 1) << 18 | slot_base << 20,
+ *   tile | part << 12 | (nparts - 1) << 16 | slot_base << 20
+ * (at most 16 parts per tile; plans are made for at most 4096 tiles per head),
  * in dispatch order; *nslots receives the partial-state slots per head.
  * Query tiles are 128 rows; a tile's keys stream in blocks of 64 keys;
  * part p of n covers blocks [p * nb / n, (p + 1) * nb / n) of the tile's nb

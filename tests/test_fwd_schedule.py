@@ -36,7 +36,7 @@ def tile_blocks(N, t, causal, Nk=None, bn=32):
 
 
 def decode(item):
-    return item & 0xFFFF, (item >> 16) & 3, ((item >> 18) & 3) + 1, item >> 20
+    return item & 0xFFF, (item >> 12) & 15, ((item >> 16) & 15) + 1, item >> 20
 
 
 def cu_throughput(k, occ):
@@ -170,9 +170,12 @@ def test_split_only_underfilled_grids():
     assert len(items) > 128 and nslots > 0
     assert _lib.schedule(16384, 2, True, 256, 3) == (items, nslots)  # cached, deterministic
     assert max(decode(it)[2] for it in _lib.schedule(1024, 1, False, 256, 3)[0]) == 4
-    # Decode (one query per head) over a long cache: every head's only tile split.
+    # Decode (one query per head) over a long cache: every head's only tile
+    # split, here into the most parts an item can have.
     items, nslots = _lib.schedule(1, 32, True, 256, 3, 32768)
-    assert len(items) == 4 and nslots == 4
+    assert len(items) == 16 and nslots == 16
+    assert sorted(decode(it)[1] for it in items) == list(range(16))
+    assert all(decode(it)[2] == 16 and decode(it)[3] == 0 for it in items)
     assert _lib.schedule(1, 32, True, 256, 3, 32768) != _lib.schedule(1, 32, True, 256, 3, 1)
 
 
