@@ -136,7 +136,7 @@ double simulate(const std::vector<Item>& items, int BH, int cus, int occ) {
 }
 
 // Items for split threshold T (blocks): tiles above T are cut into
-// min(4, ceil(nb / T)) parts. T <= 0 means no split.
+// min(FWD_MAX_PARTS, ceil(nb / T)) parts. T <= 0 means no split.
 std::vector<Item> make_items(int N, int Nk, bool causal, int bn, int T) {
   const int ntiles = (N + FWD_BM - 1) / FWD_BM;
   std::vector<Item> items;
