@@ -117,7 +117,11 @@ def cpu_baseline(x, w, budget_s: float = 12.0):
     out = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
+        # threads the oracle ran on: one process, numpy's BLAS on blas_threads
         "cores": int(blas_threads),
+        "host_cpus": os.cpu_count(),
+        "blas_threads": int(blas_threads),
+        "processes": 1,
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} heads (full N={w.N} rows each), fp64 numpy, "
                   f"{dt:.1f} s",
@@ -363,6 +367,14 @@ def mfma_probe(dev, stream, flops_target, reps, warmup=3):
             "per_launch_events": per}
 
 
+def decode_shapes(dev, stream):
+    """Decode on a batch of sequences and on one long sequence (few K/V heads
+    over a 131k-token cache, where a tile's key range is split in up to 16
+    parts)."""
+    return {"batch": decode_comparison(dev, stream),
+            "one_long_sequence": decode_comparison(dev, stream, B=1, Nk=131072)}
+
+
 def decode_comparison(dev, stream, B=8, H=32, Hkv=8, Nk=32768, d=128, reps=20):
     """Decode: one query row per head over a long K/V cache with grouped heads
     (causal, so the query sees every key). Bound by HBM, not the matrix
@@ -508,8 +520,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, resident in HBM)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "scale": w.scale},
+        "config": {"workload": W.forward_name(w), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale,
+                   "timed": "forward (fa_fwd); backward reported beside it in bwd"},
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "bound": "alu" if f32 else "mfma",
@@ -566,7 +579,7 @@ def main() -> int:
     if not args.no_bwd:
         if not args.no_split_kv:
             out["split_kv"] = split_kv_comparison(dev, stream)
-            out["decode"] = decode_comparison(dev, stream)
+            out["decode"] = decode_shapes(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
 

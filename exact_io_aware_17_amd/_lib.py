@@ -161,9 +161,10 @@ def _kv_ptr(kv_lens, B, dev):
     return kv_lens.data_ptr()
 
 
-# Zero-filled fa_fwd_ex workspaces, one per device, grown on demand: every
-# completed call leaves the counter region zero; calls that share one must be
-# stream-ordered, which holds for calls on one device's current stream.
+# Zero-filled fa_fwd_ex workspaces, one per (device, stream), grown on demand:
+# every completed call leaves the counter region zero, and calls that share a
+# workspace must be ordered, which calls on one stream are. Split forwards on
+# two streams of a device therefore never share one.
 _FWD_WS = {}
 _FWD_WS_BYTES = {}
 
@@ -185,10 +186,14 @@ def split_workspace_bytes(B: int, H: int, N: int, d: int, causal=False,
     return n
 
 
-def _fwd_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
+def _fwd_workspace(dev: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), stream)
     ws = _FWD_WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            # The old buffer may still be in use by work queued on `stream`:
+            # let the caching allocator reuse it only after that work.
+            ws.record_stream(torch.cuda.ExternalStream(stream, device=dev))
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         _FWD_WS[key] = ws
     return ws
@@ -258,7 +263,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
             if split and workspace is None:
                 need = split_workspace_bytes(B, H, Nq, d, causal, Hkv, Nk, q.dtype)
                 if need > 0:
-                    workspace = _fwd_workspace(q.device, need)
+                    workspace = _fwd_workspace(q.device, stream, need)
             if split and workspace is not None:
                 if workspace.device != q.device or not workspace.is_contiguous():
                     raise ValueError("workspace must be a contiguous tensor on q's device")

@@ -132,15 +132,16 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.causal = (mask_kind != FA_MASK_NONE);
   const int BH = B * H;
   const int cus = fa::fwd_device_cus();
-  p.bn = fa::fwd_block_keys(d, Nq, Nk, BH, p.causal != 0, cus);
+  p.bn = fa::FWD_BN;
+  std::shared_ptr<const fa::FwdPlan> held;  // keeps the plan alive until the launch
   const fa::FwdPlan* plan = &no_plan();
   if (workspace) {
     const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
-    const fa::FwdPlan& cand = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
-    const fa::FwdWorkspace w = fa::fwd_workspace_layout(cand, BH, Nq, d);
-    if (cand.nitems > 0 && workspace_bytes >= w.total) {
-      plan = &cand;
-      p.nslots = cand.nslots;
+    held = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
+    const fa::FwdWorkspace w = fa::fwd_workspace_layout(*held, BH, Nq, d);
+    if (held->nitems > 0 && workspace_bytes >= w.total) {
+      plan = held.get();
+      p.nslots = held->nslots;
       p.counters = (int*)((char*)workspace + w.counters);
       p.part_ml = (float*)((char*)workspace + w.part_ml);
       p.part_o = (float*)((char*)workspace + w.part_o);
@@ -241,10 +242,10 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
   pack_decode(H, Hkv, Nq, mask_kind);  // the launch shape fa_fwd_ex plans for
   const bool causal = (mask_kind != FA_MASK_NONE);
   const int cus = fa::fwd_device_cus();
-  const int bn = fa::fwd_block_keys(d, Nq, Nk, B * H, causal, cus);
+  const int bn = fa::FWD_BN;
   const int occ = fa::fwd_occupancy(d, bn, causal, dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16);
-  const fa::FwdPlan& plan = fa::fwd_plan(Nq, Nk, B * H, causal, bn, cus, occ);
-  return fa::fwd_workspace_layout(plan, B * H, Nq, d).total;
+  const auto plan = fa::fwd_plan(Nq, Nk, B * H, causal, bn, cus, occ);
+  return fa::fwd_workspace_layout(*plan, B * H, Nq, d).total;
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -269,17 +270,17 @@ int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int o
       mask_kind != FA_MASK_CAUSAL_STRICT)
     return FA_ERR_INVALID_ARG;
   const bool causal = mask_kind != FA_MASK_NONE;
-  const fa::FwdPlan& plan =
-      fa::fwd_plan(Nq, Nk, BH, causal, fa::fwd_block_keys(d, Nq, Nk, BH, causal, cus), cus, occ);
-  for (int i = 0; i < plan.nitems && i < max_items; ++i) items[i] = plan.item[i];
-  if (nslots) *nslots = plan.nslots;
-  return plan.nitems;
+  (void)d;  // every head dimension streams FWD_BN-key blocks
+  const auto plan = fa::fwd_plan(Nq, Nk, BH, causal, fa::FWD_BN, cus, occ);
+  for (int i = 0; i < plan->nitems && i < max_items; ++i) items[i] = plan->item[i];
+  if (nslots) *nslots = plan->nslots;
+  return plan->nitems;
 }
 
 int fa_fwd_block_keys(int B, int H, int Nq, int Nk, int d, int mask_kind) {
   const int st = check_common(B, H, H, Nq, Nk, d, 1.f, mask_kind);
   if (st != FA_OK) return st;
-  return fa::fwd_block_keys(d, Nq, Nk, B * H, mask_kind != FA_MASK_NONE, fa::fwd_device_cus());
+  return fa::FWD_BN;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

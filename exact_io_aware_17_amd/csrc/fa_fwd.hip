@@ -401,16 +401,23 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
       const float mt = pair_max(mx) * scl;  // block max, scaled (-inf if all hidden)
       const bool up = mt > m_run + TAU;
-      const float m_new = up ? mt : m_run;
-      const float corr = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
-      l_run *= corr;
-      l_bf *= corr;
+      // A sum above the bound with every block max still within TAU of its
+      // reference (many weights near 2^TAU) moves no reference: the p just
+      // computed stand. Only a moved reference, or a row with nothing
+      // visible so far (its p are not numbers), needs the rescale and the
+      // recompute.
+      if (__any(up || m_run == NEG_INF)) {
+        const float m_new = up ? mt : m_run;
+        const float corr = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 if m_run = -inf
+        l_run *= corr;
+        l_bf *= corr;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
-      m_run = m_new;
-      probabilities((m_run == NEG_INF) ? 0.f : m_run);  // nothing visible yet: p = 0
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= corr;
+        m_run = m_new;
+        probabilities((m_run == NEG_INF) ? 0.f : m_run);  // nothing visible yet: p = 0
+      }
     }
     l_run += rs;
     l_bf += lbf_blk;
@@ -463,7 +470,10 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     const buffer_rsrc rm = make_rsrc(p.part_ml + slot0 * FWD_ML_FLOATS);
     const int vo = (wave * DT * 4 * 64 + lane) * 16;  // + ((dt * 4 + g) * 64) * 16
     const int vm = (wave * 64 + lane) * 16;
-    {
+    // A wave whose rows all lie past the last query (a packed decode tile, a
+    // ragged last tile) writes no output: it neither publishes nor merges.
+    const bool live = qa < N;
+    if (live) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -481,6 +491,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     __syncthreads();
     if (s_arrival != nparts - 1) return;  // another part will merge
     if (tid == 0) atomicExch(ctr, 0);     // ready for the next call
+    if (!live) return;                    // no barrier follows
 
     // Every part, this one included, is read back and combined in part
     // order: the result does not depend on which part arrived last.

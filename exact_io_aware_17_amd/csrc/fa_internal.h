@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <memory>
+
 namespace fa {
 
 // Element types of q, k, v, o (and of the gradients).
@@ -20,7 +22,7 @@ struct FwdParams {
   int B, H, N, d;          // N: query rows per head
   int Hkv, Nk;             // K/V heads (a divisor of H) and key rows per head
   int dtype;               // DTYPE_*
-  int bn;                  // keys per streamed block (fwd_block_keys), 16-bit paths
+  int bn;                  // keys per streamed block (FWD_BN), 16-bit paths
   float scale;             // multiplies Q K^T
   float scale_log2;        // scale * log2(e), rounded once to float
   int causal;              // key j visible to query i only if j <= i + Nk - N - diag
@@ -36,11 +38,9 @@ struct FwdParams {
 
 // Forward tiling shared by the kernel and the host planner.
 constexpr int FWD_BM = 128;                 // query rows per workgroup
-// Keys per streamed block of a forward launch (the planner counts these
-// blocks): 64 for head dimensions up to 64; at d = 128, 64 (two workgroups
-// per CU) without the causal mask or for long causal rows on at most two
-// waves of workgroups, else 32 (three per CU); 32 at d = 96 and 256.
-int fwd_block_keys(int d, int Nq, int Nk, int BH, bool causal, int cus);
+// Keys per streamed block of the 16-bit forward (the planner counts these
+// blocks): 64 at every head dimension and shape.
+constexpr int FWD_BN = 64;
 // Compute units of the current device (0 if unknown; cached).
 int fwd_device_cus();
 constexpr int FWD_ML_FLOATS = 4 * 2 * FWD_BM;  // {m, l, l_bf, 0} for each of 2*BM lanes
@@ -64,10 +64,16 @@ struct FwdPlan {
 };
 
 // Balancing plan for N query rows against Nk keys, BH query heads, `cus`
-// compute units and `occ` resident workgroups per compute unit (cached; the
-// reference stays valid).
-// Blocks are of bn keys (fwd_block_keys(d)).
-const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ);
+// compute units and `occ` resident workgroups per compute unit, in blocks of
+// bn keys. Plans depend only on the tiles' block counts (so a decode loop
+// whose key count grows by one per step reuses a plan for bn steps) and are
+// kept in a bounded, least-recently-used cache; the returned plan stays
+// valid while the caller holds it.
+std::shared_ptr<const FwdPlan> fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus,
+                                        int occ);
+// Plans held by the cache (for tests of its bound) and its capacity.
+size_t fwd_plan_cache_size();
+constexpr size_t FWD_PLAN_CACHE_MAX = 128;
 // Nominal key blocks of query tile t (causal: bottom-right aligned).
 int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn);
 // Workspace layout for a plan: byte offsets of counters, part_ml, part_o and the total.

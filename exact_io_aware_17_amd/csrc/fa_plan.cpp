@@ -14,13 +14,14 @@
 // compute unit: it holds up to `occ` workgroups, its throughput depends on
 // how many are resident (a lone workgroup keeps a compute unit well under
 // full use), and a freed slot takes the next workgroup in dispatch order.
-// Plans depend only on the shape and the device's compute units and
-// occupancy, and are cached.
+// Plans depend only on the tiles' block counts and the device's compute
+// units and occupancy, and are cached (a bounded, least-recently-used cache).
 #include "fa_internal.h"
 
 #include <algorithm>
 #include <cmath>
 #include <functional>
+#include <list>
 #include <map>
 #include <memory>
 #include <mutex>
@@ -29,20 +30,6 @@
 #include <vector>
 
 namespace fa {
-
-int fwd_block_keys(int d, int Nq, int Nk, int BH, bool causal, int cus) {
-  // 64-key blocks at every head dimension: with the buffer-load DMA and the
-  // rolling operand reads they measured faster than 32-key blocks on 13 of
-  // 15 causal d = 128 shapes (up to +16 %; the two others within 2 %), by
-  // 8-17 % at d = 96 and by up to 2 % at d = 256.
-  (void)d;
-  (void)Nq;
-  (void)Nk;
-  (void)BH;
-  (void)causal;
-  (void)cus;
-  return 64;
-}
 
 int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn) {
   long long kend = Nk;
@@ -157,8 +144,8 @@ std::vector<Item> make_items(int N, int Nk, bool causal, int bn, int T) {
   return items;
 }
 
-std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ) {
-  auto plan = std::make_unique<FwdPlan>();
+std::shared_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ) {
+  auto plan = std::make_shared<FwdPlan>();
   plan->nitems = 0;
   plan->nslots = 0;
   const int ntiles = (N + FWD_BM - 1) / FWD_BM;
@@ -207,15 +194,66 @@ std::unique_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
 
 }  // namespace
 
-const FwdPlan& fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus, int occ) {
-  static std::mutex mu;
-  static std::map<std::tuple<int, int, int, bool, int, int, int>, std::unique_ptr<FwdPlan>> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_tuple(N, Nk, BH, causal, bn, cus, occ);
-  auto it = cache.find(key);
-  if (it != cache.end()) return *it->second;
-  auto res = cache.emplace(key, build_plan(N, Nk, BH, causal, bn, cus, occ));
-  return *res.first->second;
+namespace {
+
+// Plan cache: keyed on what a plan depends on (the block count of every query
+// tile, the heads, compute units and occupancy), least recently used first
+// out once FWD_PLAN_CACHE_MAX plans are held.
+typedef std::tuple<int, int, int, std::vector<int>> PlanKey;
+struct PlanCache {
+  std::mutex mu;
+  std::list<PlanKey> order;  // most recently used first
+  std::map<PlanKey, std::pair<std::shared_ptr<const FwdPlan>, std::list<PlanKey>::iterator>> map;
+};
+PlanCache& plan_cache() {
+  static PlanCache c;
+  return c;
+}
+
+}  // namespace
+
+std::shared_ptr<const FwdPlan> fwd_plan(int N, int Nk, int BH, bool causal, int bn, int cus,
+                                        int occ) {
+  const int ntiles = (N + FWD_BM - 1) / FWD_BM;
+  std::vector<int> nbs;
+  if (ntiles <= 0xfff) {
+    nbs.reserve((size_t)ntiles);
+    for (int t = 0; t < ntiles; ++t) nbs.push_back(fwd_tile_blocks(N, Nk, t, causal, bn));
+  } else {
+    nbs.push_back(-ntiles);  // too many tiles to plan for: never split
+  }
+  PlanKey key(BH, cus, occ, std::move(nbs));
+  PlanCache& c = plan_cache();
+  {
+    std::lock_guard<std::mutex> lock(c.mu);
+    auto it = c.map.find(key);
+    if (it != c.map.end()) {
+      c.order.splice(c.order.begin(), c.order, it->second.second);
+      return it->second.first;
+    }
+  }
+  // Built outside the lock (a pure function of the key); a concurrent
+  // builder of the same key keeps whichever entry landed first.
+  std::shared_ptr<const FwdPlan> plan = build_plan(N, Nk, BH, causal, bn, cus, occ);
+  std::lock_guard<std::mutex> lock(c.mu);
+  auto it = c.map.find(key);
+  if (it != c.map.end()) {
+    c.order.splice(c.order.begin(), c.order, it->second.second);
+    return it->second.first;
+  }
+  c.order.push_front(key);
+  c.map.emplace(std::move(key), std::make_pair(plan, c.order.begin()));
+  while (c.map.size() > FWD_PLAN_CACHE_MAX) {
+    c.map.erase(c.order.back());
+    c.order.pop_back();
+  }
+  return plan;
+}
+
+size_t fwd_plan_cache_size() {
+  PlanCache& c = plan_cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  return c.map.size();
 }
 
 FwdWorkspace fwd_workspace_layout(const FwdPlan& plan, int BH, int N, int d) {

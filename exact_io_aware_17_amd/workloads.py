@@ -73,6 +73,11 @@ def with_shape(w: Workload, **changes) -> Workload:
     return dataclasses.replace(w, **changes)
 
 
+def forward_name(w: Workload) -> str:
+    """The workload's forward alone (what a forward throughput line measures)."""
+    return w.name.replace("causal fwd+bwd", "causal fwd")
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Draw the workload's inputs on the CPU, following the recipe in the module doc.
 

@@ -35,9 +35,9 @@
  * Layout: q, o (and dout, dq) are contiguous [B, H, Nq, d]; k, v (and dk, dv)
  * contiguous [B, Hkv, Nk, d] (d innermost); lse is contiguous [B, H, Nq]
  * float32. Pointers are device pointers allocated by the caller (the library
- * allocates and frees no device memory; on the host it caches per-shape work
- * plans and per-device occupancy, guarded by a mutex). Tensor and workspace
- * base pointers must be 16-byte aligned.
+ * allocates and frees no device memory; on the host it keeps a bounded cache
+ * of work plans and per-device occupancy, guarded by mutexes). Tensor and
+ * workspace base pointers must be 16-byte aligned.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.

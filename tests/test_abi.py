@@ -214,3 +214,4 @@ def test_block_keys_rule_and_errors():
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 0) == 64
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 1) == 64
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 256, 2) == 64
+

@@ -13,6 +13,7 @@ the next workgroup in dispatch order), and the chosen plan must shorten it by
 the planner's required margin.
 """
 import heapq
+import os
 import math
 
 import pytest
@@ -190,3 +191,30 @@ def test_schedule_argument_errors():
     assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, -1, 3, None, 0, None) == INV
     assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, 256, -3, None, 0, None) == INV
     assert lib.fa_fwd_schedule(128, 128, 1, 128, 1, 256, 3, None, 4, None) == INV
+
+
+def _rss_bytes():
+    with open("/proc/self/statm") as f:
+        return int(f.read().split()[1]) * os.sysconf("SC_PAGE_SIZE")
+
+
+def test_plan_cache_stays_bounded_over_a_decode_loop():
+    """A decode loop plans one more key per step: 20,000 consecutive key
+    counts (313 distinct block counts, more than the cache holds) must not
+    grow the host memory by a plan per step (about 2 KiB each, 40 MB in
+    all), and key counts with the same block count share one plan."""
+    import ctypes
+    lib = _lib.load()
+    buf = (ctypes.c_uint32 * 4096)()
+    ns = ctypes.c_int(0)
+    lib.fa_fwd_schedule(1, 1, 64, 128, 1, 256, 2, buf, 4096, ctypes.byref(ns))
+    r0 = _rss_bytes()
+    for nk in range(1, 20001):
+        n = lib.fa_fwd_schedule(1, nk, 64, 128, 1, 256, 2, buf, 4096, ctypes.byref(ns))
+        assert n >= 0
+    assert _rss_bytes() - r0 < 8 * 2 ** 20
+    a = _lib.schedule(1, 64, True, 256, 2, Nk=4097, d=128)
+    b = _lib.schedule(1, 64, True, 256, 2, Nk=4160, d=128)   # same 65 blocks of 64 keys
+    c = _lib.schedule(1, 64, True, 256, 2, Nk=4161, d=128)   # 66 blocks
+    assert a == b
+    assert a[0] and c[0]
