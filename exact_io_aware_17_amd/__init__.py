@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     default_scale,
     dtype_code,
     fwd,
+    fwd_noalloc,
     load,
     mask_kind,
     schedule,

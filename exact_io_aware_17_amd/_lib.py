@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -38,6 +38,8 @@ SIGNATURES = {
     "fa_fwd_ex_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "fa_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                        ctypes.c_size_t, _vp]),
+    "fa_fwd_ex_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                               _vp, _vp]),
     "fa_fwd_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -272,6 +274,38 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
             st = lib.fa_fwd_ex(*tensors, B, H, Hkv, Nq, Nk, d, code, float(scale), mask, kvp,
                                ws_ptr, ws_bytes, stream)
     _check(fn_name, st)
+    return out, lse
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,
+                scale: Optional[float] = None, kv_lens: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fa_fwd_ex_noalloc: the split-KV forward of fwd(split=True) with its
+    workspace in the library's per-device scratch (no device allocation by
+    the library; `out` and `lse`, if given, make the call allocation-free
+    here too). Calls on one device must be ordered (they share the scratch)."""
+    B, H, Hkv, Nq, Nk, d = _check_qkv(q, k, v)
+    code = dtype_code(q.dtype)
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must match q")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    kvp = _kv_ptr(kv_lens, B, q.device)
+    lib = load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv,
+                                   Nq, Nk, d, code, float(scale), mask_kind(causal), kvp,
+                                   _stream(q.device))
+    _check("fa_fwd_ex_noalloc", st)
     return out, lse
 
 

@@ -24,7 +24,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 PROBE_LIB = os.path.join(HERE, "libfa_probe.so")
 
-SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_bwd.hip",
+           "fa_noalloc.hip"]
 PROBE_SOURCES = ["probe/fa_probe.hip"]
 
 # Per-source extra flags. The 16-bit forward keeps its MFMA accumulators in

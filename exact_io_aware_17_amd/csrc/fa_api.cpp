@@ -8,6 +8,9 @@
 
 #include "fa_internal.h"
 
+static_assert(fa::NOALLOC_SCRATCH_BYTES == FA_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size the library holds");
+
 namespace {
 
 bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
@@ -69,9 +72,14 @@ const fa::FwdPlan& no_plan() {
   return plan;
 }
 
+// Where a forward's split-KV workspace comes from: the caller, or the
+// library's per-device scratch (fa_fwd_ex_noalloc).
+enum WorkspaceSource { WS_CALLER, WS_SCRATCH };
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream,
+               WorkspaceSource source = WS_CALLER) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!workspace && workspace_bytes) return FA_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
@@ -135,7 +143,27 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.bn = fa::FWD_BN;
   std::shared_ptr<const fa::FwdPlan> held;  // keeps the plan alive until the launch
   const fa::FwdPlan* plan = &no_plan();
-  if (workspace) {
+  if (source == WS_SCRATCH) {
+    // Every argument is valid: take the plan, check that its workspace fits
+    // the scratch, then find this device's scratch and clear the counters
+    // the plan uses (the scratch keeps whatever the last call left).
+    const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
+    held = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
+    const fa::FwdWorkspace w = fa::fwd_workspace_layout(*held, BH, Nq, d);
+    if (w.total > fa::NOALLOC_SCRATCH_BYTES) return FA_ERR_UNSUPPORTED;
+    if (held->nitems > 0) {
+      char* ws = (char*)fa::noalloc_scratch();
+      if (!ws) return FA_ERR_HIP;
+      plan = held.get();
+      p.nslots = held->nslots;
+      p.counters = (int*)(ws + w.counters);
+      p.part_ml = (float*)(ws + w.part_ml);
+      p.part_o = (float*)(ws + w.part_o);
+      const int ntiles = (Nq + fa::FWD_BM - 1) / fa::FWD_BM;
+      if (fa::clear_ints(p.counters, BH * ntiles, (hipStream_t)stream) != hipSuccess)
+        return FA_ERR_HIP;
+    }
+  } else if (workspace) {
     const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
     held = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(*held, BH, Nq, d);
@@ -253,6 +281,13 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, dtype, scale, mask_kind, kv_lens,
                     workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
+                      const int32_t* kv_lens, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, dtype, scale, mask_kind, kv_lens,
+                    nullptr, 0, stream, WS_SCRATCH);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

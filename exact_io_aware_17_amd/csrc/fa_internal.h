@@ -115,4 +115,12 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
+// fa_fwd_ex_noalloc's workspace: a device array of this many bytes per GPU
+// (fa_noalloc.hip). noalloc_scratch() returns the current device's copy
+// (nullptr if its address cannot be obtained); clear_ints() enqueues a
+// kernel that zeroes n ints.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+void* noalloc_scratch();
+hipError_t clear_ints(int* p, int n, hipStream_t stream);
+
 }  // namespace fa

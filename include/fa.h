@@ -35,9 +35,11 @@
  * Layout: q, o (and dout, dq) are contiguous [B, H, Nq, d]; k, v (and dk, dv)
  * contiguous [B, Hkv, Nk, d] (d innermost); lse is contiguous [B, H, Nq]
  * float32. Pointers are device pointers allocated by the caller (the library
- * allocates and frees no device memory; on the host it keeps a bounded cache
- * of work plans and per-device occupancy, guarded by mutexes). Tensor and
- * workspace base pointers must be 16-byte aligned.
+ * allocates and frees no device memory; fa_fwd_ex_noalloc's scratch is a
+ * device array reserved when the library's code is loaded onto a GPU. On the
+ * host it keeps a bounded cache of work plans and per-device occupancy,
+ * guarded by mutexes). Tensor and workspace base pointers must be 16-byte
+ * aligned.
  *
  * Asynchrony: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum {
   FA_OK = 0,
@@ -153,6 +155,30 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
               int mask_kind, const int32_t* kv_lens, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): fa_fwd_ex
+ * with its split-KV workspace taken from a scratch array that the library
+ * holds on each device instead of a caller-provided one. Same arguments,
+ * results and plans as fa_fwd_ex given a large enough workspace (bitwise the
+ * same outputs); no device memory is allocated or freed.
+ * The scratch is FA_NOALLOC_SCRATCH_BYTES per GPU, reserved when the
+ * library's device code is loaded onto that GPU and held until the process
+ * ends. Every call on a GPU shares it and it keeps the last call's contents:
+ * each call that splits first clears the arrival counters it uses (a small
+ * kernel on `stream`, never a memset). Calls that overlap on one GPU race
+ * for the scratch and give wrong results: order them (one stream, or
+ * synchronised).
+ * Errors as fa_fwd_ex; FA_ERR_UNSUPPORTED when the split plan for these
+ * sizes needs more than FA_NOALLOC_SCRATCH_BYTES of workspace
+ * (fa_fwd_ex_workspace_bytes tells), FA_ERR_HIP when the scratch's device
+ * address cannot be obtained or a launch fails.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
+                      int mask_kind, const int32_t* kv_lens, void* stream);
 
 /*
  * The same contract with float32 q, k, v, o (float32 arithmetic throughout).

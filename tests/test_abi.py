@@ -59,12 +59,16 @@ def _fwd(fn="fa_fwd", q=A, k=A + SZ, v=A + 2 * SZ, o=A + 3 * SZ, lse=A + 4 * SZ,
     if fn.startswith("fa_fwd_ex"):
         code = int(fn.split(":")[1]) if ":" in fn else _lib.FA_DTYPE_BF16
         code = code if dtype is None else dtype
+        if fn.startswith("fa_fwd_ex_noalloc"):
+            return lib.fa_fwd_ex_noalloc(q, k, v, o, lse, B, H, Hkv, N, Nk, d, code, scale, mask,
+                                         kv, None)
         return lib.fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, Nk, d, code, scale, mask, kv, ws,
                              ws_bytes, None)
     return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, scale, mask, kv, None)
 
 
-EX = ["fa_fwd_ex", "fa_fwd_ex:1", "fa_fwd_ex:2"]
+EX = ["fa_fwd_ex", "fa_fwd_ex:1", "fa_fwd_ex:2", "fa_fwd_ex_noalloc", "fa_fwd_ex_noalloc:1",
+      "fa_fwd_ex_noalloc:2"]
 
 
 @pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"] + EX)
@@ -95,6 +99,7 @@ def test_dtype_argument_errors():
     INV = _lib.FA_ERR_INVALID_ARG
     assert _fwd("fa_fwd_ex", dtype=3) == INV
     assert _fwd("fa_fwd_ex", dtype=-1) == INV
+    assert _fwd("fa_fwd_ex_noalloc", dtype=3) == INV
     lib = _lib.load()
     assert lib.fa_fwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, 3, 1) == 0
     assert lib.fa_fwd_ex_workspace_bytes(1, 2, 2, 16384, 16384, 128, 2, 1) == 0  # fp32: no split
@@ -215,3 +220,16 @@ def test_block_keys_rule_and_errors():
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 128, 1) == 64
     assert lib.fa_fwd_block_keys(1, 1, 16, 16, 256, 2) == 64
 
+
+def test_noalloc_scratch_size_is_the_header_constant():
+    with open(os.path.join(ROOT, "include", "fa.h")) as f:
+        text = f.read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 64 << 20
+    with open(os.path.join(ROOT, "exact_io_aware_17_amd", "csrc", "fa_noalloc.hip")) as f:
+        src = f.read()
+    # The scratch is a file-scope device array whose address the host takes
+    # with hipGetSymbolAddress; the array's name is not passed anywhere else.
+    assert "static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES]" in src
+    assert src.count("scratch)") == 1 and "HIP_SYMBOL(scratch)" in src
+    assert "hipMalloc" not in src and "hipMemset" not in src
