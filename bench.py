@@ -16,7 +16,11 @@ softmax, the comparison path, not part of libfa) is timed on the same inputs
 
 Prints ONE JSON line. Timing uses HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes to
-libfa). The roofline's kernel duration is the average launch duration over
+libfa). The device raises its clock over the first tens of milliseconds of
+load after idling, so after the W warmup launches K launches are timed once
+as they come ("cold_start", reported only), then forward launches keep the
+device busy for --settle-ms ("settle"), then W warmup launches and the timed
+region whose mean is the value. The roofline's kernel duration is the average launch duration over
 the timed region (its two events divided by the K launches it holds); an
 event pair around each of K further launches is reported beside it
 ("per_launch_events", mean, median and min), and so is a third set of K
@@ -245,6 +249,69 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
     return 0
 
 
+def summarize_trace(trace_dir: str, bench_file: str, command: str) -> int:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
+    script: the libfa kernels' statistics, and the metric forward's kernel
+    durations per phase of the run (cold start, settle, timed region, ...),
+    found by dispatch order from the counts the profiled bench line reports."""
+    import csv
+    import glob
+
+    line = json.loads(open(bench_file).read().strip().splitlines()[-1])
+    stats_f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace_f = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if len(stats_f) != 1 or len(trace_f) != 1:
+        print("expected one kernel_stats.csv and one kernel_trace.csv", file=sys.stderr)
+        return 1
+    names = {"fwd_kernel": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+             "bwd_prep": "bwd_prep_kernel", "mfma_peak": "mfma_peak_kernel"}
+    rows = []
+    for r in csv.DictReader(open(stats_f[0])):
+        if any(t in r["Name"] for t in names):
+            rows.append(r)
+    metric_kernel = None
+    for r in csv.DictReader(open(trace_f[0])):
+        if FWD_KERNEL_TAG in r["Kernel_Name"]:
+            metric_kernel = r["Kernel_Name"]  # the first forward dispatch is the metric's
+            break
+    durs = [(int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            for r in csv.DictReader(open(trace_f[0])) if r["Kernel_Name"] == metric_kernel]
+    durs = [d for _, d in sorted(durs)]
+    W, K = line["warmup"], line["steps"]
+    S = line["settle"]["launches"]
+    phases = [("warm-up", W), ("cold start (K launches)", K), ("settle", S), ("warm-up", W),
+              ("timed region", K), ("per-launch event pairs", K), ("after a 512 MiB fill", K)]
+    out = ["# rocprofv3 kernel trace: libfa kernels, " + line["config"]["workload"], "",
+           "Command (repository root, one MI355X):", "", "    " + command, "",
+           "Kernel statistics (`*_kernel_stats.csv`, libfa kernels):", "",
+           "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                   f"{r['MinNs']} | {r['MaxNs']} |")
+    out += ["", f"Metric forward (`{metric_kernel[:90]}`), kernel durations by phase of the run "
+            "(dispatch order, from `*_kernel_trace.csv`):", "",
+            "| phase | launches | mean us | min us | max us |", "|---|---|---|---|---|"]
+    i = 0
+    timed = None
+    for name, n in phases:
+        seg = durs[i:i + n]
+        i += n
+        if not seg:
+            break
+        if name == "timed region":
+            timed = sum(seg) / len(seg)
+        out.append(f"| {name} | {len(seg)} | {sum(seg) / len(seg):.1f} | {min(seg):.1f} | "
+                   f"{max(seg):.1f} |")
+    flops = line["roofline"]["flops_per_launch"]
+    out += ["", f"The profiled bench line: value {line['value']} TFLOP/s, ms_per_step "
+            f"{line['ms_per_step']} (the timed region's events, gaps between launches included); "
+            f"the trace's timed-region mean kernel time {timed:.1f} us is "
+            f"{flops / (timed * 1e-6) / 1e12:.0f} TFLOP/s of kernel time, "
+            f"{100 * timed * 1e-3 / line['ms_per_step']:.1f} % of ms_per_step."]
+    print("\n".join(out))
+    return 0
+
+
 def naive_forward(q, k, v, scale, causal):
     """The unfused path the pages contrast with: S = scale Q K^T and
     P = softmax(S) written to and read back from device memory (bf16), then
@@ -306,6 +373,35 @@ def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
         ms = a.elapsed_time(b) / reps
         res[name] = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
     return res
+
+
+def timed_region(fn, steps, stream):
+    """Mean ms per launch of `steps` launches back to back between two events."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def settle_clock(fn, settle_ms, stream, group=20):
+    """Launch `fn` in groups of `group` back to back until at least
+    `settle_ms` of wall time has passed. The device raises its clock over the
+    first tens of milliseconds of load after idling (the same forward runs
+    about 15-20 % slower per launch during that ramp), so a rate taken right
+    after a short warmup measures the ramp rather than the kernel. Returns
+    what was run and the per-launch time of the first and last groups."""
+    times = []
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms or len(times) < 2:
+        times.append(timed_region(fn, group, stream))
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "launches": group * len(times),
+            "first_group_ms_per_launch": round(times[0], 5),
+            "last_group_ms_per_launch": round(times[-1], 5)}
 
 
 def timing_summary(ms, flops):
@@ -413,6 +509,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="wall time of forward launches run before the W warmup steps so that "
+                         "the timed region starts at the device's sustained clock (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-split-kv", action="store_true",
@@ -429,9 +528,14 @@ def main() -> int:
                          "the committed traffic summary")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command recorded in the traffic summary")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LINE_FILE"),
+                    help="markdown summary of a rocprofv3 --kernel-trace --stats run of this "
+                         "script, with the bench line it printed")
     args = ap.parse_args()
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.traffic_command)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace, args.traffic_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -461,6 +565,17 @@ def main() -> int:
     def fwd_once():
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, kv_lens=kv, out=o, lse=lse)
 
+    for _ in range(args.warmup):
+        fwd_once()
+    torch.cuda.synchronize()
+
+    # Cold start: K launches right after the W warmup launches, with the
+    # device clock still ramping up from idle (reported, not the value).
+    cold = timed_region(fwd_once, args.steps, stream)
+    # Settle: keep the device busy with the same launches until its clock
+    # has left the ramp (about 30 ms of load on the devices measured), then
+    # W warmup launches again and the timed region.
+    settle = settle_clock(fwd_once, args.settle_ms, stream)
     for _ in range(args.warmup):
         fwd_once()
     torch.cuda.synchronize()
@@ -538,6 +653,12 @@ def main() -> int:
             "kernel_ms_mean": round(ms_step, 5),
             "algorithmic_hbm_bytes": W.fwd_bytes(w.B, w.H, w.N, w.d, 2),
         },
+        "cold_start": {"what": "K launches right after the first W warmup launches, the device "
+                               "clock still ramping up from idle (not the value)",
+                       "ms_per_step": round(cold, 5),
+                       "tflops": round(flops / (cold * 1e-3) / 1e12, 2)},
+        "settle": dict({"what": "forward launches run between the cold-start region and the W "
+                                "warmup launches before the timed region"}, **settle),
         "per_launch_events": dict(
             {"what": "event pair around each of K launches after the timed region"},
             **timing_summary(per_launch, flops)),

@@ -73,8 +73,15 @@ using namespace dev;
 constexpr int NW = 4;         // waves per workgroup
 constexpr int BM = 32 * NW;   // queries per workgroup
 static_assert(BM == FWD_BM, "workgroup tile matches the host planner");
-constexpr float TAU = 8.0f;   // allowed lag of the reference max (log2 units)
-constexpr float P_BOUND = 256.0f;  // 2^TAU: no p exceeds it while the lag holds
+// Allowed lag of the reference max (log2 units), per element type. While the
+// lag holds every weight p is at most 2^TAU: fp16 weights must stay far below
+// its largest finite value (65504 = 2^16 - 2^5), so TAU = 8 there; bf16 has
+// fp32's exponent range, and with TAU = 32 no weight, lane sum (at most 64
+// weights), row sum or accumulator (at most 2^31 keys of weight 2^32 times
+// |V|) approaches the fp32 range, while rows of widely spread scores move
+// their reference far less often.
+template <typename T>
+constexpr float lag_tau() { return std::is_same<T, _Float16>::value ? 8.0f : 32.0f; }
 
 #ifndef FA_PRIO_MFMA
 #define FA_PRIO_MFMA 1  // wave priority (s_setprio) during the MFMA phases
@@ -97,6 +104,8 @@ template <typename T, int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdParams p, FwdPlan plan) {
   typedef Elem<T> E;
   typedef typename E::x8 x8;
+  constexpr float TAU = lag_tau<T>();
+  constexpr float P_BOUND = (float)(1ull << (int)TAU);  // 2^TAU
   constexpr int ROWB = D * 2;                 // bytes per K/V row
   constexpr int TILE = BN * ROWB;             // bytes per K or V tile
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row

@@ -173,9 +173,10 @@ def test_two_d_direct(golden, dtype, d):
 @pytest.mark.parametrize("x", [10.0, 100.0])
 def test_lag_rescale_on_cell_f(golden, dtype, d, x):
     """Cell F's row [x, 0] with its keys in two blocks, the 0 first: the
-    reference max then jumps by x natural units (10 and 100, both more than
-    the kernel's lag of 8 log2 units = 5.55 natural units), so the block
-    rescale branch runs, with factor e^-x."""
+    reference max then jumps by x natural units. The kernel moves its
+    reference when a block's max exceeds it by more than its lag, 8 log2
+    units (5.55 natural units) for fp16 and 32 (22.2) for bf16: x = 10 runs
+    the rescale branch (factor e^-10) in fp16, x = 100 in both."""
     ex = {e["id"]: e for e in golden["row_examples"]}[f"cell_F_x{int(x)}"]
     keys = [(0, 0.0, [20.0]), (BLOCK + 7, x, [10.0])]
     q, k, v = _build(keys, 2 * BLOCK, d, dtype)
