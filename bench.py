@@ -312,6 +312,59 @@ def summarize_trace(trace_dir: str, bench_file: str, command: str) -> int:
     return 0
 
 
+def summarize_counters(dirs, workload: int) -> int:
+    """Median, over the workload's three forward dispatches of a --profile-run,
+    of every counter in the rocprofv3 --pmc output directories `dirs`, and
+    the per-wave, per-key-block readings (JSON)."""
+    import csv
+    import glob
+
+    from exact_io_aware_17_amd import workloads as W
+
+    w = W.BY_ID[workload]
+    vals = {}
+    kernel = None
+    for d in dirs:
+        per = {}  # dispatch id -> counter -> summed value
+        names = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if FWD_KERNEL_TAG not in r["Kernel_Name"]:
+                    continue
+                i = int(r["Dispatch_Id"])
+                names[i] = r["Kernel_Name"]
+                c = per.setdefault(i, {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        first = sorted(per)[:3]  # --profile-run: the workload's three forward launches come first
+        kernel = names[first[0]]
+        for name in per[first[0]]:
+            vals[name] = statistics.median(per[i][name] for i in first)
+    waves = vals.get("SQ_WAVES")
+    out = {"workload": w.name, "kernel": kernel, "median_of_3_dispatches": vals}
+    if waves and "SQ_INSTS_MFMA" in vals:
+        mfma_per_block = 2 * (w.d // 16) * 2  # S and P V: (D/16) x 2 key tiles each per 64-key block
+        blocks = vals["SQ_INSTS_MFMA"] / waves / mfma_per_block
+        out["key_blocks_per_wave"] = round(blocks, 2)
+        per_block = lambda k: round(vals[k] / waves / blocks, 1) if k in vals else None
+        out["per_wave_and_block"] = {
+            "mfma": per_block("SQ_INSTS_MFMA"),
+            "valu_other_than_mfma": round((vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / waves / blocks, 1)
+            if "SQ_INSTS_VALU" in vals else None,
+            "exp2": per_block("SQ_INSTS_VALU_TRANS_F32"),
+            "lds": per_block("SQ_INSTS_LDS"),
+            "salu": per_block("SQ_INSTS_SALU")}
+        if "SQ_WAVE_CYCLES" in vals:
+            out["share_of_wave_time"] = {k: round(vals[k] / vals["SQ_WAVE_CYCLES"], 3)
+                                         for k in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                                                   "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS")
+                                         if k in vals}
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in vals and "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            out["valu_coissued_share_of_mfma_busy"] = round(
+                vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / vals["SQ_VALU_MFMA_BUSY_CYCLES"], 3)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def naive_forward(q, k, v, scale, causal):
     """The unfused path the pages contrast with: S = scale Q K^T and
     P = softmax(S) written to and read back from device memory (bf16), then
@@ -531,7 +584,12 @@ def main() -> int:
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LINE_FILE"),
                     help="markdown summary of a rocprofv3 --kernel-trace --stats run of this "
                          "script, with the bench line it printed")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="median SQ counters of the workload's forward in rocprofv3 --pmc runs "
+                         "of --profile-run (one directory per counter pass)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.traffic_command)
     if args.summarize_trace:
