@@ -115,3 +115,86 @@ def test_cpu_baseline_only_times_the_oracle_without_a_gpu():
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
     assert cb["sample"].startswith("1 of 1 heads")
     assert "extrapolated_all_heads_s" not in cb  # the whole workload was timed
+
+
+FWD = "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELi64ELb1EEEvNS_9FwdParamsENS_7FwdPlanE"
+
+
+def test_trace_summary_finds_the_timed_region(tmp_path, capsys):
+    """The timed region's launches are found by dispatch order from the counts
+    the bench line reports (warm-up, cold start, settle, warm-up, timed)."""
+    W, K, S = 5, 20, 40
+    durs = [140.0] * W + [160.0] * K + [135.0] * S + [131.0] * W + [130.0] * K + [129.0] * K
+    d = tmp_path / "trace" / "vm"
+    d.mkdir(parents=True)
+    with open(d / "1_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                           "End_Timestamp"])
+        wr.writeheader()
+        t = 1000
+        for i, us in enumerate(durs):
+            wr.writerow({"Dispatch_Id": 2 * i + 1, "Kernel_Name": FWD, "Start_Timestamp": t,
+                         "End_Timestamp": t + int(us * 1000)})
+            wr.writerow({"Dispatch_Id": 2 * i + 2, "Kernel_Name": "other", "Start_Timestamp": t,
+                         "End_Timestamp": t + 1})
+            t += 10 ** 6
+    with open(d / "1_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        wr.writeheader()
+        wr.writerow({"Name": FWD, "Calls": len(durs), "AverageNs": 1.0, "MinNs": 1, "MaxNs": 2})
+    line = {"warmup": W, "steps": K, "settle": {"launches": S}, "value": 1.0,
+            "ms_per_step": 0.132, "config": {"workload": "w"},
+            "roofline": {"flops_per_launch": 137438953472.0}}
+    (tmp_path / "line.json").write_text("noise\n" + json.dumps(line) + "\n")
+    assert bench.summarize_trace(str(tmp_path / "trace"), str(tmp_path / "line.json"), "cmd") == 0
+    out = capsys.readouterr().out
+    assert "| timed region | 20 | 130.0 | 130.0 | 130.0 |" in out
+    assert "| cold start (K launches) | 20 | 160.0 |" in out
+    assert "| settle | 40 | 135.0 |" in out
+    assert "98.5 % of ms_per_step" in out
+
+
+def test_counter_summary_medians_and_per_block_readings(tmp_path, capsys):
+    """Medians over the workload's three forward dispatches (the first three of
+    the forward kernel), counters of one pass summed over their rows."""
+    vals = {1: 4096.0, 2: 4096.0, 3: 4096.0}
+    rows = []
+    for i, name in ((1, FWD), (2, "copy"), (3, FWD), (4, FWD), (5, FWD)):
+        for c, v in (("SQ_WAVES", 4096.0), ("SQ_INSTS_MFMA", 4259840.0 + i),
+                     ("SQ_INSTS_VALU", 23650304.0), ("SQ_WAVE_CYCLES", 100.0)):
+            half = v / 2  # two rows per counter (e.g. two shader engines)
+            rows += [(i, name, c, half), (i, name, c, half)]
+    d = tmp_path / "pmc" / "vm"
+    d.mkdir(parents=True)
+    with open(d / "1_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
+        wr.writeheader()
+        for i, n, c, v in rows:
+            wr.writerow({"Dispatch_Id": i, "Kernel_Name": n, "Counter_Name": c,
+                         "Counter_Value": v})
+    assert bench.summarize_counters([str(tmp_path / "pmc")], 5) == 0
+    out = json.loads(capsys.readouterr().out)
+    assert out["median_of_3_dispatches"]["SQ_WAVES"] == 4096.0
+    assert out["median_of_3_dispatches"]["SQ_INSTS_MFMA"] == 4259840.0 + 3  # dispatches 1, 3, 4
+    # d = 128: 32 MFMAs per wave and 64-key block
+    assert out["key_blocks_per_wave"] == pytest.approx(32.5, abs=1e-3)
+    assert out["per_wave_and_block"]["mfma"] == pytest.approx(32.0)
+    assert out["per_wave_and_block"]["valu_other_than_mfma"] == pytest.approx(145.7, abs=0.1)
+
+
+def test_settle_runs_for_the_requested_time(monkeypatch):
+    calls = []
+
+    def fake_region(fn, steps, stream):
+        calls.append(steps)
+        import time
+        time.sleep(0.002)
+        return 0.15 if len(calls) == 1 else 0.13
+
+    monkeypatch.setattr(bench, "timed_region", fake_region)
+    s = bench.settle_clock(lambda: None, 20.0, None, group=20)
+    assert s["ms"] >= 20.0 and s["launches"] == 20 * len(calls) >= 40
+    assert s["first_group_ms_per_launch"] == 0.15 and s["last_group_ms_per_launch"] == 0.13
+    s = bench.settle_clock(lambda: None, 0.0, None)
+    assert s["launches"] >= 40  # at least two groups, so first and last are reported
