@@ -78,7 +78,7 @@ enum WorkspaceSource { WS_CALLER, WS_SCRATCH };
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream,
+               const int32_t* kv_lens, void* workspace, size_t workspace_bytes, hipStream_t stream,
                WorkspaceSource source = WS_CALLER) {
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!workspace && workspace_bytes) return FA_ERR_INVALID_ARG;
@@ -131,7 +131,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.part_o = nullptr;
   p.bn = 0;
   if (f32) {
-    hipError_t e = fa::launch_fwd_f32(p, (hipStream_t)stream);
+    hipError_t e = fa::launch_fwd_f32(p, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   pack_decode(H, Hkv, Nq, mask_kind);
@@ -160,7 +160,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
       p.part_ml = (float*)(ws + w.part_ml);
       p.part_o = (float*)(ws + w.part_o);
       const int ntiles = (Nq + fa::FWD_BM - 1) / fa::FWD_BM;
-      if (fa::clear_ints(p.counters, BH * ntiles, (hipStream_t)stream) != hipSuccess)
+      if (fa::clear_ints(p.counters, BH * ntiles, stream) != hipSuccess)
         return FA_ERR_HIP;
     }
   } else if (workspace) {
@@ -175,14 +175,14 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
       p.part_o = (float*)((char*)workspace + w.part_o);
     }
   }
-  hipError_t e = fa::launch_fwd(p, *plan, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd(p, *plan, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
                int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-               const int32_t* kv_lens, void* stream) {
+               const int32_t* kv_lens, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
@@ -232,7 +232,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind != FA_MASK_NONE);
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
-  hipError_t e = fa::launch_bwd(p, (hipStream_t)stream);
+  hipError_t e = fa::launch_bwd(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -258,7 +258,7 @@ const char* fa_status_string(int status) {
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+           int d, float scale, int mask_kind, const int32_t* kv_lens, hipStream_t stream) {
   return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, FA_DTYPE_BF16, scale, mask_kind, kv_lens,
                     nullptr, 0, stream);
 }
@@ -278,20 +278,20 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-              const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+              const int32_t* kv_lens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, dtype, scale, mask_kind, kv_lens,
                     workspace, workspace_bytes, stream);
 }
 
 int fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-                      const int32_t* kv_lens, void* stream) {
+                      const int32_t* kv_lens, hipStream_t stream) {
   return fwd_common(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, dtype, scale, mask_kind, kv_lens,
                     nullptr, 0, stream, WS_SCRATCH);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
-               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+               int N, int d, float scale, int mask_kind, const int32_t* kv_lens, hipStream_t stream) {
   return fwd_common(q, k, v, o, lse, B, H, H, N, N, d, FA_DTYPE_F32, scale, mask_kind, kv_lens,
                     nullptr, 0, stream);
 }
@@ -325,7 +325,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
-           int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream) {
+           int d, float scale, int mask_kind, const int32_t* kv_lens, hipStream_t stream) {
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, H, N, N, d, FA_DTYPE_BF16,
                     scale, mask_kind, kv_lens, stream);
 }
@@ -333,7 +333,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
               int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
-              const int32_t* kv_lens, void* stream) {
+              const int32_t* kv_lens, hipStream_t stream) {
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk, d, dtype,
                     scale, mask_kind, kv_lens, stream);
 }

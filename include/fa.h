@@ -65,6 +65,16 @@
 extern "C" {
 #endif
 
+/* HIP's stream handle. hip_runtime_api.h defines hipStream_t as a pointer to
+ * the opaque struct ihipStream_t; this header repeats that definition when
+ * HIP's own header has not been included yet, so it builds without the HIP
+ * headers and a hipStream_t passes to every call unchanged (NULL = the null
+ * stream). Identical typedefs may be repeated (C11, C++). */
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+#endif
+
 #define FA_ABI_VERSION 8
 
 typedef enum {
@@ -99,14 +109,14 @@ typedef enum {
  *             may be NULL when the caller does not need it
  *   scale   : multiplies Q K^T; normally 1/sqrt(d)
  *   kv_lens : device int32 [B] valid key counts, or NULL
- *   stream  : hipStream_t
+ *   stream  : the HIP stream the kernels are enqueued on (NULL = null stream)
  * Products Q K^T and P V run on bf16 matrix cores with float32 accumulation;
  * P is rounded to bfloat16 before the P V product. One workgroup computes
  * each block of 128 query rows over all of its visible keys.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int mask_kind,
-           const int32_t* kv_lens, void* stream);
+           const int32_t* kv_lens, hipStream_t stream);
 
 /*
  * Bytes of workspace fa_fwd_ex needs for these sizes on the current device
@@ -154,7 +164,7 @@ size_t fa_fwd_ex_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, i
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
               int mask_kind, const int32_t* kv_lens, void* workspace,
-              size_t workspace_bytes, void* stream);
+              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
@@ -178,14 +188,14 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
 #define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
 int fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
-                      int mask_kind, const int32_t* kv_lens, void* stream);
+                      int mask_kind, const int32_t* kv_lens, hipStream_t stream);
 
 /*
  * The same contract with float32 q, k, v, o (float32 arithmetic throughout).
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
-               const int32_t* kv_lens, void* stream);
+               const int32_t* kv_lens, hipStream_t stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (caller-allocated,
@@ -209,7 +219,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, void* workspace,
            int B, int H, int N, int d, float scale, int mask_kind,
-           const int32_t* kv_lens, void* stream);
+           const int32_t* kv_lens, hipStream_t stream);
 
 /*
  * fa_bwd for bf16 or fp16 tensors (dtype FA_DTYPE_BF16 or FA_DTYPE_F16;
@@ -225,7 +235,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dout, void* dq, void* dk, void* dv, void* workspace,
               int B, int H, int Hkv, int Nq, int Nk, int d, int dtype, float scale,
-              int mask_kind, const int32_t* kv_lens, void* stream);
+              int mask_kind, const int32_t* kv_lens, hipStream_t stream);
 
 /*
  * Host-only view of fa_fwd_ex's work plan (no device call): for Nq query

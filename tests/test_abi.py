@@ -233,3 +233,33 @@ def test_noalloc_scratch_size_is_the_header_constant():
     assert "static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES]" in src
     assert src.count("scratch)") == 1 and "HIP_SYMBOL(scratch)" in src
     assert "hipMalloc" not in src and "hipMemset" not in src
+
+
+@pytest.mark.parametrize("order", ["alone_c11", "hip_first", "fa_first"])
+def test_header_stream_type_matches_hip(tmp_path, order):
+    """fa.h builds without HIP's headers (C11) and, with them included before
+    or after it, takes a hipStream_t as the stream argument unchanged."""
+    import shutil
+    import subprocess
+    inc = os.path.join(ROOT, "include")
+    if order == "alone_c11":
+        src = tmp_path / "t.c"
+        src.write_text('#include "fa.h"\nint main(void) { hipStream_t s = 0; (void)s; '
+                       'return fa_abi_version() > 0 ? 0 : 1; }\n')
+        cc = shutil.which("gcc") or shutil.which("cc")
+        if not cc:
+            pytest.skip("no C compiler")
+        cmd = [cc, "-std=c11", "-Wall", "-Werror", "-I", inc, "-c", str(src), "-o",
+               str(tmp_path / "t.o")]
+    else:
+        hip = "#include <hip/hip_runtime.h>\n"
+        fa = '#include "fa.h"\n'
+        body = ("int f(hipStream_t s) { return fa_fwd(0, 0, 0, 0, 0, 1, 1, 1, 64, 1.f, 0, 0, s); }\n")
+        src = tmp_path / "t.cpp"
+        src.write_text((hip + fa if order == "hip_first" else fa + hip) + body)
+        hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+        if not os.path.exists(hipcc):
+            pytest.skip("no hipcc")
+        cmd = [hipcc, "-std=c++17", "-I", inc, "-c", str(src), "-o", str(tmp_path / "t.o")]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
