@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     FA_ERR_HIP,
     FA_ERR_INVALID_ARG,
     FA_ERR_UNSUPPORTED,
+    FA_FWD_ORDER_HEAVY_FIRST,
+    FA_FWD_ORDER_PAIRED,
     FA_MASK_CAUSAL,
     FA_MASK_CAUSAL_STRICT,
     FA_MASK_NONE,
@@ -31,4 +33,5 @@ from ._lib import (  # noqa: F401
     schedule,
     split_workspace_bytes,
     status_string,
+    tile_order,
 )

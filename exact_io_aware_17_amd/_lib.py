@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -47,6 +47,7 @@ SIGNATURES = {
     "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                        _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
+    "fa_fwd_tile_order": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "fa_fwd_block_keys": (_i, [_i, _i, _i, _i, _i, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
@@ -213,6 +214,22 @@ def schedule(N: int, BH: int, causal, cus: int, occ: int, Nk: Optional[int] = No
     if n < 0:
         raise FaError("fa_fwd_schedule", n, status_string(n))
     return [int(buf[i]) for i in range(n)], int(ns.value)
+
+
+FA_FWD_ORDER_HEAVY_FIRST = 0
+FA_FWD_ORDER_PAIRED = 1
+
+
+def tile_order(N: int, BH: int, d: int, causal, Nk: Optional[int] = None,
+               dtype: torch.dtype = torch.bfloat16, cus: int = 0, occ: int = 0) -> int:
+    """fa_fwd_tile_order: FA_FWD_ORDER_HEAVY_FIRST or FA_FWD_ORDER_PAIRED for
+    N query rows against Nk keys (default N); cus = occ = 0 asks for the
+    current device's compute units and occupancy."""
+    n = int(load().fa_fwd_tile_order(N, N if Nk is None else Nk, BH, d, dtype_code(dtype),
+                                     mask_kind(causal), cus, occ))
+    if n < 0:
+        raise FaError("fa_fwd_tile_order", n, status_string(n))
+    return n
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal=False,

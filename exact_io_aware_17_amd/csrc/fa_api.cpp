@@ -125,6 +125,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind != FA_MASK_NONE);
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
+  p.pair = 0;
   p.nslots = 0;
   p.counters = nullptr;
   p.part_ml = nullptr;
@@ -141,13 +142,13 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   const int BH = B * H;
   const int cus = fa::fwd_device_cus();
   p.bn = fa::FWD_BN;
+  const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
   std::shared_ptr<const fa::FwdPlan> held;  // keeps the plan alive until the launch
   const fa::FwdPlan* plan = &no_plan();
   if (source == WS_SCRATCH) {
     // Every argument is valid: take the plan, check that its workspace fits
     // the scratch, then find this device's scratch and clear the counters
     // the plan uses (the scratch keeps whatever the last call left).
-    const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
     held = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(*held, BH, Nq, d);
     if (w.total > fa::NOALLOC_SCRATCH_BYTES) return FA_ERR_UNSUPPORTED;
@@ -164,7 +165,6 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
         return FA_ERR_HIP;
     }
   } else if (workspace) {
-    const int occ = fa::fwd_occupancy(d, p.bn, p.causal != 0, p.dtype);
     held = fa::fwd_plan(Nq, Nk, BH, p.causal != 0, p.bn, cus, occ);
     const fa::FwdWorkspace w = fa::fwd_workspace_layout(*held, BH, Nq, d);
     if (held->nitems > 0 && workspace_bytes >= w.total) {
@@ -175,6 +175,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
       p.part_o = (float*)((char*)workspace + w.part_o);
     }
   }
+  if (plan->nitems == 0 && fa::fwd_pair_tiles(Nq, Nk, d, BH, p.causal != 0, cus, occ)) p.pair = 1;
   hipError_t e = fa::launch_fwd(p, *plan, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -310,6 +311,23 @@ int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int o
   for (int i = 0; i < plan->nitems && i < max_items; ++i) items[i] = plan->item[i];
   if (nslots) *nslots = plan->nslots;
   return plan->nitems;
+}
+
+int fa_fwd_tile_order(int Nq, int Nk, int BH, int d, int dtype, int mask_kind, int cus, int occ) {
+  if (Nq <= 0 || Nk <= 0 || BH <= 0 || d <= 0 || cus < 0 || occ < 0) return FA_ERR_INVALID_ARG;
+  if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL &&
+      mask_kind != FA_MASK_CAUSAL_STRICT)
+    return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  const bool causal = mask_kind != FA_MASK_NONE;
+  if (cus == 0 && occ == 0) {
+    cus = fa::fwd_device_cus();
+    occ = fa::fwd_occupancy(d, fa::FWD_BN, causal,
+                            dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16);
+  }
+  return fa::fwd_pair_tiles(Nq, Nk, d, BH, causal, cus, occ) ? FA_FWD_ORDER_PAIRED
+                                                             : FA_FWD_ORDER_HEAVY_FIRST;
 }
 
 int fa_fwd_block_keys(int B, int H, int Nq, int Nk, int d, int mask_kind) {

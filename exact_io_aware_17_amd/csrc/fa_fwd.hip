@@ -48,6 +48,14 @@
 //    straddle the diagonal or the padding length apply a mask.
 //  * A row with no visible key keeps l = 0 and is written as O = 0 and
 //    lse = -inf ("Worked examples", Cell D2).
+//  * Tile order (causal): by default one tile per workgroup, the tiles that
+//    see the most keys first. When one head's K and V outgrow an XCD's L2,
+//    the host selects the paired instance instead: a workgroup takes tile
+//    ntiles-1-r with its keys ascending, then tile r with its keys
+//    descending. The online recurrence is exact in any block order ("The
+//    Flash Attention"; "Exercises", a common reference), every pair streams
+//    about ntiles+1 tiles' worth of blocks, and the pairs of a head read the
+//    same two blocks at a time, so K and V are fetched about once per XCD.
 //  * Load balance: a host plan may cut a tile's key range into up to 16
 //    parts processed by different workgroups. Each part stores its partial
 //    state (unnormalised O, reference max, both sums; fp32) and counts its
@@ -100,8 +108,11 @@ constexpr int fwd_wg_per_cu(int D, int BN) {
 // Head dimensions with kernel instances.
 #define FA_FOR_EACH_D(X) X(32) X(64) X(96) X(128) X(256)
 
-template <typename T, int D, int BN, bool CAUSAL>
+// PAIRED (causal only): each workgroup takes a pair of query tiles (see the
+// work item below) instead of one.
+template <typename T, int D, int BN, bool CAUSAL, bool PAIRED>
 __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdParams p, FwdPlan plan) {
+  static_assert(CAUSAL || !PAIRED, "pairs balance causal tiles");
   typedef Elem<T> E;
   typedef typename E::x8 x8;
   constexpr float TAU = lag_tau<T>();
@@ -144,42 +155,55 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
   // ---- work item ----
   const int N = p.N;
   const int ntiles = (N + BM - 1) / BM;
-  // Item-major order: workgroup id w takes item w / (B*H) of head w % (B*H).
-  // Workgroups are dispatched in id order, round-robin over the 8 XCDs, so
-  // every XCD sees the heaviest items first and, when B*H is a multiple of
-  // 8, the items of a fixed set of heads, whose K and V then share its L2.
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  const int rank = blockIdx.x / BH;
-  int tile, part = 0, nparts = 1, slot_base = 0;
-  if (plan.nitems > 0) {
-    const unsigned it = plan.item[rank];
-    tile = (int)(it & 0xfffu);
-    part = (int)((it >> 12) & 15u);
-    nparts = (int)((it >> 16) & 15u) + 1;
-    slot_base = (int)(it >> 20);
+  // Workgroups are dispatched in id order, round-robin over the 8 XCDs
+  // (id % 8), each with its own L2.
+  int bh, tile0, ntile = 1, part = 0, nparts = 1, slot_base = 0;
+  if constexpr (PAIRED) {
+    // Paired causal tiles: item r is tile ntiles-1-r (keys ascending) then,
+    // if different, tile r (keys descending). Every item streams about
+    // ntiles+1 tiles' worth of blocks, and the workgroups of one head read
+    // only two key positions at any time: all heavy tiles are at block t,
+    // all light tiles at the block t mirrors. When B*H is a multiple of 8,
+    // XCD x takes the heads x, x+8, x+16, ... (the same heads as in the
+    // item-major order, so per-batch key lengths load every XCD alike) and
+    // runs their items head by head, keeping few heads' K and V in its L2.
+    const int npairs = (ntiles + 1) / 2;
+    int r;
+    if ((BH & 7) == 0) {
+      const int k = blockIdx.x >> 3;
+      bh = (blockIdx.x & 7) + 8 * (k / npairs);
+      r = k % npairs;
+    } else {
+      bh = blockIdx.x % BH;
+      r = blockIdx.x / BH;
+    }
+    tile0 = ntiles - 1 - r;
+    if (tile0 != r) ntile = 2;
   } else {
-    tile = CAUSAL ? ntiles - 1 - rank : rank;  // causal: the latest rows see the most keys
+    // Item-major order: workgroup id w takes item w / (B*H) of head
+    // w % (B*H), so every XCD sees the heaviest items first and, when B*H
+    // is a multiple of 8, the items of a fixed set of heads, whose K and V
+    // then share its L2.
+    bh = blockIdx.x % BH;
+    const int rank = blockIdx.x / BH;
+    if (plan.nitems > 0) {
+      const unsigned it = plan.item[rank];
+      tile0 = (int)(it & 0xfffu);
+      part = (int)((it >> 12) & 15u);
+      nparts = (int)((it >> 16) & 15u) + 1;
+      slot_base = (int)(it >> 20);
+    } else {
+      tile0 = CAUSAL ? ntiles - 1 - rank : rank;  // causal: the latest rows see the most keys
+    }
   }
   const int b = bh / p.H;
-  const int q0 = tile * BM;
   const int Nk = p.Nk;
   // Causal: key visible iff key <= query + shift (queries are the last N of
   // the Nk positions; the strict mask also hides the query's own position).
   const int shift = CAUSAL ? Nk - N - p.diag : 0;
-
   int kvlen = Nk;
   if (p.kv_lens) kvlen = min(max(p.kv_lens[b], 0), Nk);
-  int kend = kvlen;
-  if (CAUSAL) kend = max(min(kend, q0 + BM + shift), 0);
-  const int nblk = (kend + BN - 1) / BN;  // visible blocks
-  // This item's block range: its share of the tile's nominal (unpadded)
-  // blocks, clipped to the visible ones.
-  const int nbn = (max(CAUSAL ? min(Nk, q0 + BM + Nk - N) : Nk, 0) + BN - 1) / BN;
-  const int jbeg = part * nbn / nparts;
-  const int jend = min((part + 1) * nbn / nparts, nblk);
-  const int qa = q0 + wave * 32;  // first query of this wave
-  const int qrow = qa + n;
 
   const size_t head = (size_t)bh * N * D;  // Q, O rows of this head
   const size_t kvhead = ((size_t)b * p.Hkv + (bh % p.H) / (p.H / p.Hkv)) * Nk * D;
@@ -187,15 +211,11 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
   const T* __restrict__ K = (const T*)p.k + kvhead;
   const T* __restrict__ V = (const T*)p.v + kvhead;
 
-  // ---- Q^T fragments: lane (n, h) holds query qrow, dims 16c + 8h .. +8 ----
-  x8 qf[DC];
-  {
-    const int qrow_c = min(qrow, N - 1);
-#pragma unroll
-    for (int c = 0; c < DC; ++c)
-      qf[c] = *(const x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  // Per-tile state, set at the start of each tile of the item.
+  int tile, q0;        // query tile and its first row
+  int jbeg, jend;      // this item's key blocks of the tile: [jbeg, jend)
+  int qa, qrow;        // first query of this wave; query of this lane
+  bool started;        // the wave has processed a block of this tile
 
   // ---- K/V block stream, HBM -> LDS ----
   // Per-lane source offsets inside a block (bytes), fixed for the kernel: a
@@ -232,7 +252,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
   // operand reads of the LDS by count while a DMA is in flight.
   auto issue_block = [&](int j, auto stage) {
     constexpr int SD = decltype(stage)::value;
-    if (j >= jend) return;
+    if ((PAIRED && j < jbeg) || j >= jend) return;  // only a descending stream runs below jbeg
     const int key0 = j * BN;
     char* ks = SD == 0 ? kbuf0 : kbuf1;
     char* vs = SD == 0 ? vbuf0 : vbuf1;
@@ -289,22 +309,22 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     voff[dt] = vrow * ROWB + vslot<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
   }
 
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
-  float m_run = NEG_INF;  // reference max (scaled log2 units)
-  float l_run = 0.f;      // this lane's share of sum p (fp32)
-  float l_bf = 0.f;       // the same over the rounded (16-bit) p used by P V
+  x8 qf[DC];              // Q^T fragments: lane (n, h) holds query qrow, dims 16c + 8h .. +8
+  f32x16 acc[DT];         // O^T, unnormalised
+  float m_run;            // reference max (scaled log2 units)
+  float l_run;            // this lane's share of sum p (fp32)
+  float l_bf;             // the same over the rounded (16-bit) p used by P V
   const float scl = p.scale_log2;
 
   // One key block: the stage (LDS buffer) is a compile-time constant, so
-  // every LDS operand offset is an immediate. Block j uses stage
-  // (j - jbeg) % 2; the DMA of block j+1 goes to the other stage.
-  auto step = [&](int j, auto stage) {
+  // every LDS operand offset is an immediate. The c-th block of a tile's
+  // stream uses stage c % 2; block jnext, the one after it, goes to the
+  // other stage.
+  auto step = [&](int j, int jnext, auto stage) {
     constexpr int ST = decltype(stage)::value;
     // Block j has landed once this wave's DMAs are done (its only
     // outstanding vector-memory operations) and every wave has passed the
-    // barrier, which also frees the other stage, read in block j-1.
+    // barrier, which also frees the other stage, read in the previous block.
     wait_vmem();
     __syncthreads();
     const int key0 = j * BN;
@@ -345,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // issue overlaps their drain instead of delaying the first K read, and
     // with no LDS DMA in flight during the K reads the compiler waits for
     // each read by count (lgkmcnt(n)) rather than for all of them.
-    issue_block(j + 1, std::integral_constant<int, 1 - ST>());
+    issue_block(jnext, std::integral_constant<int, 1 - ST>());
     if (skip) return;
     __builtin_amdgcn_s_setprio(0);
     // ---- mask (only blocks that straddle the diagonal or kv_len) ----
@@ -388,10 +408,14 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
         pf[kc] = __builtin_bit_cast(x8, w);
       }
     };
-    if (j == jbeg) {
-      // First block of the item: there is nothing to rescale yet, so the
-      // reference max is simply the block's row max (-inf for a row with no
-      // visible key, whose p are then 0) and the lag check below passes.
+    // A descending stream's first blocks straddle the diagonal, so a wave may
+    // skip some before its first; an ascending one starts at jbeg.
+    if (PAIRED ? !started : j == jbeg) {
+      // First block of the tile this wave processes: there is nothing to
+      // rescale yet, so the reference max is simply the block's row max
+      // (-inf for a row with no visible key, whose p are then 0) and the lag
+      // check below passes.
+      started = true;
       float mx = NEG_INF;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
@@ -455,116 +479,153 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     }
   };
 
-  issue_block(jbeg, std::integral_constant<int, 0>());
-  __builtin_amdgcn_sched_barrier(0);
-  for (int j = jbeg; j < jend; j += 2) {
-    step(j, std::integral_constant<int, 0>());
-    if (j + 1 < jend) step(j + 1, std::integral_constant<int, 1>());
-  }
-  __builtin_amdgcn_s_setprio(0);
-  wait_vmem();  // no DMA may still target this workgroup's LDS at exit
-
-  // ---- split item: publish the partial state; the last arrival merges ----
-  if (nparts > 1) {
-    // Slot layout (fp32): accumulators as [wave][dt][r/4][lane][r%4] (every
-    // 16-byte access of a wave covers 1 KB contiguously), then per lane
-    // {m, l, l_bf, 0}. Written and read with device-coherent 16-byte buffer
-    // accesses (they bypass the per-XCD L2 caches), so no cache-wide
-    // write-back or invalidation is needed; completing this wave's stores
-    // before the barrier orders them before the arrival count.
-    constexpr int SLOT_O = BM * D * 4;              // bytes of accumulators per slot
-    constexpr int SLOT_ML = FWD_ML_FLOATS * 4;      // bytes of row statistics per slot
-    const size_t slot0 = (size_t)bh * p.nslots + slot_base;
-    const buffer_rsrc ro = make_rsrc(p.part_o + slot0 * (BM * D));
-    const buffer_rsrc rm = make_rsrc(p.part_ml + slot0 * FWD_ML_FLOATS);
-    const int vo = (wave * DT * 4 * 64 + lane) * 16;  // + ((dt * 4 + g) * 64) * 16
-    const int vm = (wave * 64 + lane) * 16;
-    // A wave whose rows all lie past the last query (a packed decode tile, a
-    // ragged last tile) writes no output: it neither publishes nor merges.
-    const bool live = qa < N;
-    if (live) {
+  for (int it = 0; it < ntile; ++it) {
+    tile = it ? ntiles - 1 - tile0 : tile0;
+    q0 = tile * BM;
+    int kend = kvlen;
+    if (CAUSAL) kend = max(min(kend, q0 + BM + shift), 0);
+    const int nblk = (kend + BN - 1) / BN;  // visible blocks
+    // This item's block range: its share of the tile's nominal (unpadded)
+    // blocks, clipped to the visible ones.
+    const int nbn = (max(CAUSAL ? min(Nk, q0 + BM + Nk - N) : Nk, 0) + BN - 1) / BN;
+    jbeg = part * nbn / nparts;
+    jend = min((part + 1) * nbn / nparts, nblk);
+    qa = q0 + wave * 32;
+    qrow = qa + n;
+    {
+      const int qrow_c = min(qrow, N - 1);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
-          store_coherent16(v, ro, part * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
-        }
-      const f32x4 st = {m_run, l_run, l_bf, 0.f};
-      store_coherent16(st, rm, part * SLOT_ML + vm);
+      for (int c = 0; c < DC; ++c)
+        qf[c] = *(const x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
     }
-    wait_vmem();
-    __syncthreads();
-    int* ctr = p.counters + (size_t)bh * ntiles + tile;
-    if (tid == 0) s_arrival = atomicAdd(ctr, 1);
-    __syncthreads();
-    if (s_arrival != nparts - 1) return;  // another part will merge
-    if (tid == 0) atomicExch(ctr, 0);     // ready for the next call
-    if (!live) return;                    // no barrier follows
-
-    // Every part, this one included, is read back and combined in part
-    // order: the result does not depend on which part arrived last.
-    // The row statistics are read twice (max first, then the sums), so any
-    // number of parts merges in the same registers.
-    float m_all = NEG_INF;
-    for (int q = 0; q < nparts; ++q) m_all = fmaxf(m_all, load_coherent16(rm, q * SLOT_ML + vm)[0]);
-    float l_sum = 0.f, lbf_sum = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
-    for (int q = 0; q < nparts; ++q) {
-      const f32x4 stat = load_coherent16(rm, q * SLOT_ML + vm);
-      const float m_q = stat[0];
-      const float c = (m_q == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_q - m_all);
-      l_sum = fmaf(c, stat[1], l_sum);
-      lbf_sum = fmaf(c, stat[2], lbf_sum);
+    m_run = NEG_INF;
+    l_run = 0.f;
+    l_bf = 0.f;
+    started = false;
+    // A second tile: every wave has finished reading both stages of the
+    // first before stage 0 is refilled.
+    if (it) __syncthreads();
+    // The first tile streams its blocks in ascending order, the second in
+    // descending order.
+    const int dir = it ? -1 : 1;
+    const int jfirst = it ? jend - 1 : jbeg;
+    const int nb = jend - jbeg;
+    issue_block(jfirst, std::integral_constant<int, 0>());
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < nb; c += 2) {
+      const int j = jfirst + c * dir;
+      step(j, j + dir, std::integral_constant<int, 0>());
+      if (c + 1 < nb) step(j + dir, j + 2 * dir, std::integral_constant<int, 1>());
+    }
+    __builtin_amdgcn_s_setprio(0);
+    wait_vmem();  // no DMA may still target this workgroup's LDS at exit
+
+    // ---- split item: publish the partial state; the last arrival merges ----
+    if (nparts > 1) {
+      // Slot layout (fp32): accumulators as [wave][dt][r/4][lane][r%4] (every
+      // 16-byte access of a wave covers 1 KB contiguously), then per lane
+      // {m, l, l_bf, 0}. Written and read with device-coherent 16-byte buffer
+      // accesses (they bypass the per-XCD L2 caches), so no cache-wide
+      // write-back or invalidation is needed; completing this wave's stores
+      // before the barrier orders them before the arrival count.
+      constexpr int SLOT_O = BM * D * 4;              // bytes of accumulators per slot
+      constexpr int SLOT_ML = FWD_ML_FLOATS * 4;      // bytes of row statistics per slot
+      const size_t slot0 = (size_t)bh * p.nslots + slot_base;
+      const buffer_rsrc ro = make_rsrc(p.part_o + slot0 * (BM * D));
+      const buffer_rsrc rm = make_rsrc(p.part_ml + slot0 * FWD_ML_FLOATS);
+      const int vo = (wave * DT * 4 * 64 + lane) * 16;  // + ((dt * 4 + g) * 64) * 16
+      const int vm = (wave * 64 + lane) * 16;
+      // A wave whose rows all lie past the last query (a packed decode tile, a
+      // ragged last tile) writes no output: it neither publishes nor merges.
+      const bool live = qa < N;
+      if (live) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
+            store_coherent16(v, ro, part * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
+          }
+        const f32x4 st = {m_run, l_run, l_bf, 0.f};
+        store_coherent16(st, rm, part * SLOT_ML + vm);
+      }
+      wait_vmem();
+      __syncthreads();
+      int* ctr = p.counters + (size_t)bh * ntiles + tile;
+      if (tid == 0) s_arrival = atomicAdd(ctr, 1);
+      __syncthreads();
+      if (s_arrival != nparts - 1) return;  // another part will merge
+      if (tid == 0) atomicExch(ctr, 0);     // ready for the next call
+      if (!live) return;                    // no barrier follows
+
+      // Every part, this one included, is read back and combined in part
+      // order: the result does not depend on which part arrived last.
+      // The row statistics are read twice (max first, then the sums), so any
+      // number of parts merges in the same registers.
+      float m_all = NEG_INF;
+      for (int q = 0; q < nparts; ++q) m_all = fmaxf(m_all, load_coherent16(rm, q * SLOT_ML + vm)[0]);
+      float l_sum = 0.f, lbf_sum = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) zero(acc[dt]);
+      for (int q = 0; q < nparts; ++q) {
+        const f32x4 stat = load_coherent16(rm, q * SLOT_ML + vm);
+        const float m_q = stat[0];
+        const float c = (m_q == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(m_q - m_all);
+        l_sum = fmaf(c, stat[1], l_sum);
+        lbf_sum = fmaf(c, stat[2], lbf_sum);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = load_coherent16(ro, q * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[dt][4 * g + e] = fmaf(c, v[e], acc[dt][4 * g + e]);
+          }
+      }
+      m_run = m_all;
+      l_run = l_sum;
+      l_bf = lbf_sum;
+    }
+
+    // ---- finalize ----
+    const float l_tot = pair_sum(l_run);
+    const float l_o = pair_sum(l_bf);
+    const bool empty = (l_tot == 0.f);
+    const float inv = empty ? 0.f : 1.f / l_o;
+    if (qrow < N) {
+      T* O = (T*)p.o + head + (size_t)qrow * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 v = load_coherent16(ro, q * SLOT_O + vo + (dt * 4 + g) * 64 * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[dt][4 * g + e] = fmaf(c, v[e], acc[dt][4 * g + e]);
+          u32x2 w;
+          w[0] = E::pack(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
+          w[1] = E::pack(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+          *(u32x2*)(O + dt * 32 + 8 * g + 4 * h) = w;
         }
-    }
-    m_run = m_all;
-    l_run = l_sum;
-    l_bf = lbf_sum;
-  }
-
-  // ---- finalize ----
-  const float l_tot = pair_sum(l_run);
-  const float l_o = pair_sum(l_bf);
-  const bool empty = (l_tot == 0.f);
-  const float inv = empty ? 0.f : 1.f / l_o;
-  if (qrow < N) {
-    T* O = (T*)p.o + head + (size_t)qrow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = E::pack(acc[dt][4 * g] * inv, acc[dt][4 * g + 1] * inv);
-        w[1] = E::pack(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
-        *(u32x2*)(O + dt * 32 + 8 * g + 4 * h) = w;
+      if (h == 0 && p.lse) {
+        p.lse[(size_t)bh * N + qrow] = empty ? NEG_INF : (m_run + log2f(l_tot)) * LN2;
       }
-    if (h == 0 && p.lse) {
-      p.lse[(size_t)bh * N + qrow] = empty ? NEG_INF : (m_run + log2f(l_tot)) * LN2;
     }
-  }
+  }  // tiles of the item
 }
 
 template <typename T, int D, int BN>
 hipError_t launch_d(const FwdParams& p, const FwdPlan& plan, hipStream_t stream) {
   const long long ntiles = (p.N + BM - 1) / BM;
-  const long long items = plan.nitems > 0 ? plan.nitems : ntiles;
+  const bool paired = p.causal && p.pair && plan.nitems == 0;
+  const long long items = plan.nitems > 0 ? plan.nitems : (paired ? (ntiles + 1) / 2 : ntiles);
   const long long grid = (long long)p.B * p.H * items;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BN, true>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p, plan);
+  const dim3 g((unsigned)grid), blk(NW * 64);
+  if (paired)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, true>), g, blk, 0, stream, p, plan);
+  else if (p.causal)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, true, false>), g, blk, 0, stream, p, plan);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BN, false>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       stream, p, plan);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BN, false, false>), g, blk, 0, stream, p, plan);
   return hipGetLastError();
 }
 
@@ -572,7 +633,7 @@ template <typename T, int D, int BN, bool CAUSAL>
 int occupancy() {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, BN, CAUSAL>), NW * 64,
+          &per, reinterpret_cast<const void*>(&fwd_kernel<T, D, BN, CAUSAL, false>), NW * 64,
           0) != hipSuccess)
     return 0;
   return per;

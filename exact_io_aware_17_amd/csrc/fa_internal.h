@@ -27,6 +27,9 @@ struct FwdParams {
   float scale_log2;        // scale * log2(e), rounded once to float
   int causal;              // key j visible to query i only if j <= i + Nk - N - diag
   int diag;                // 0: causal (j <= i), 1: strict causal (j < i)
+  // Causal without a split plan: 1 if each workgroup takes the pair of
+  // query tiles (ntiles-1-r, r) (fwd_pair_tiles), 0 for one tile each.
+  int pair;
   // Split work items (used only with a plan of nitems > 0): per (b, h)
   // nslots partial states, each BM rows of unnormalised O (fp32) plus the
   // row max and both row sums, and one arrival counter per query tile.
@@ -76,6 +79,17 @@ size_t fwd_plan_cache_size();
 constexpr size_t FWD_PLAN_CACHE_MAX = 128;
 // Nominal key blocks of query tile t (causal: bottom-right aligned).
 int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn);
+// L2 cache of one XCD of the target device (gfx950: 4 MB per XCD).
+constexpr long long FWD_L2_BYTES = 4ll << 20;
+// Whether an unsplit causal forward pairs its query tiles: tile ntiles-1-r
+// (keys ascending) then tile r (keys descending) in one workgroup, so that
+// every workgroup streams ntiles+1 tiles' worth of blocks and the workgroups
+// of a head read two key positions at a time. Chosen when one head's K and
+// V (2 * Nk * d 16-bit elements) are at least one XCD's L2, where streaming
+// every tile from key 0 re-fetches K and V in proportion to N, and the
+// paired grid still fills every resident slot (BH * ceil(ntiles / 2) >=
+// cus * occ).
+bool fwd_pair_tiles(int N, int Nk, int d, int BH, bool causal, int cus, int occ);
 // Workspace layout for a plan: byte offsets of counters, part_ml, part_o and the total.
 struct FwdWorkspace {
   size_t counters, part_ml, part_o, total;

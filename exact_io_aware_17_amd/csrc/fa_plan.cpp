@@ -38,6 +38,13 @@ int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn) {
   return (int)((kend + bn - 1) / bn);
 }
 
+bool fwd_pair_tiles(int N, int Nk, int d, int BH, bool causal, int cus, int occ) {
+  const long long ntiles = ((long long)N + FWD_BM - 1) / FWD_BM;
+  if (!causal || ntiles < 2 || Nk <= 0 || d <= 0 || BH <= 0 || cus <= 0 || occ <= 0) return false;
+  if (2ll * Nk * d * 2 < FWD_L2_BYTES) return false;
+  return (long long)BH * ((ntiles + 1) / 2) >= (long long)cus * occ;
+}
+
 namespace {
 
 // Costs in units of one streamed key block of a workgroup on a full compute

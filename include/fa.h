@@ -75,7 +75,7 @@ struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
 
 typedef enum {
   FA_OK = 0,
@@ -112,7 +112,9 @@ typedef enum {
  *   stream  : the HIP stream the kernels are enqueued on (NULL = null stream)
  * Products Q K^T and P V run on bf16 matrix cores with float32 accumulation;
  * P is rounded to bfloat16 before the P V product. One workgroup computes
- * each block of 128 query rows over all of its visible keys.
+ * each block of 128 query rows over all of its visible keys; under the
+ * causal mask with long key rows one workgroup computes two such blocks
+ * (fa_fwd_tile_order).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int mask_kind,
@@ -253,6 +255,37 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  */
 int fa_fwd_schedule(int Nq, int Nk, int BH, int d, int mask_kind, int cus, int occ,
                     uint32_t* items, int max_items, int* nslots);
+
+/* Assignment of query tiles (128 rows) to workgroups; fa_fwd_tile_order. */
+typedef enum {
+  FA_FWD_ORDER_HEAVY_FIRST = 0,  /* one tile per workgroup, the tiles that see
+                                    the most keys dispatched first; keys
+                                    stream in ascending order */
+  FA_FWD_ORDER_PAIRED = 1        /* causal: workgroup r takes tile
+                                    ntiles-1-r (keys ascending) and then tile
+                                    r (keys descending), so every workgroup
+                                    streams about ntiles+1 tiles' worth of
+                                    key blocks and those of one head read the
+                                    same two key blocks at a time */
+} fa_fwd_order;
+
+/*
+ * Host-side view of the tile order fa_fwd and fa_fwd_ex use for Nq query
+ * rows against Nk keys, BH = B*H query heads, head dimension d, dtype
+ * (FA_DTYPE_BF16 or FA_DTYPE_F16) and mask_kind, on `cus` compute units with
+ * `occ` resident workgroups per compute unit (cus = occ = 0: those of the
+ * current device, which makes a device query; otherwise no device call).
+ * When fa_fwd_ex splits key ranges (a workspace and fa_fwd_schedule > 0),
+ * the split plan is used instead. Pairs are used under a causal mask when
+ * one head's K and V (2 * Nk * d elements of 2 bytes) are at least 4 MB,
+ * the L2 cache of one XCD, and BH * ceil(Nq / 128) / 2 workgroups still fill
+ * every resident slot: streaming every tile from key 0 then fetches K and V
+ * again from memory in proportion to Nq, while pairs keep the fetched bytes
+ * a constant multiple of the inputs.
+ * Returns an fa_fwd_order value, FA_ERR_INVALID_ARG for invalid arguments,
+ * or FA_ERR_UNSUPPORTED for FA_DTYPE_F32.
+ */
+int fa_fwd_tile_order(int Nq, int Nk, int BH, int d, int dtype, int mask_kind, int cus, int occ);
 
 /*
  * Keys per streamed block that fa_fwd / fa_fwd_ex use for these sizes on the

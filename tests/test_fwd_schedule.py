@@ -218,3 +218,68 @@ def test_plan_cache_stays_bounded_over_a_decode_loop():
     c = _lib.schedule(1, 64, True, 256, 2, Nk=4161, d=128)   # 66 blocks
     assert a == b
     assert a[0] and c[0]
+
+
+# ---- tile order (fa_fwd_tile_order; host only with explicit cus, occ) ----
+
+L2_BYTES = 4 << 20   # one XCD's L2 cache, the header's threshold
+
+
+def expected_order(Nq, Nk, BH, d, causal, cus, occ):
+    """The header's rule: pairs under a causal mask when one head's K and V
+    (2 * Nk * d two-byte elements) are at least one XCD's L2 and the pairs
+    still fill every resident slot."""
+    ntiles = -(-Nq // BM)
+    paired = (causal and ntiles >= 2 and 2 * Nk * d * 2 >= L2_BYTES
+              and BH * (-(-ntiles // 2)) >= cus * occ)
+    return _lib.FA_FWD_ORDER_PAIRED if paired else _lib.FA_FWD_ORDER_HEAVY_FIRST
+
+
+@pytest.mark.parametrize("Nq,Nk,BH,d,causal,cus,occ,want", [
+    (4096, 4096, 32, 128, True, 256, 2, "heavy"),     # K+V of a head 2 MB: fits the L2
+    (8192, 8192, 32, 128, True, 256, 2, "paired"),    # 4 MB: exactly the L2
+    (8191, 8191, 32, 128, True, 256, 2, "heavy"),     # one key short of it
+    (8192, 8192, 32, 128, False, 256, 2, "heavy"),    # no mask: tiles cost the same
+    (16384, 16384, 32, 64, True, 256, 3, "paired"),
+    (8192, 8192, 32, 64, True, 256, 3, "heavy"),
+    (16384, 16384, 4, 128, True, 256, 2, "heavy"),    # 256 pairs for 512 slots
+    (16384, 16384, 8, 128, True, 256, 2, "paired"),   # 512 pairs fill 512 slots
+    (16300, 16300, 8, 128, True, 256, 2, "paired"),   # odd tile count (128 tiles -> 64 pairs)
+    (128, 1 << 20, 4096, 128, True, 256, 2, "heavy"), # a single tile
+    (256, 8192, 512, 128, True, 256, 2, "paired"),    # Nq < Nk
+    (4096, 4096, 16, 256, True, 256, 1, "paired"),    # d = 256: 4 MB at N = 4096
+])
+def test_tile_order_rule(Nq, Nk, BH, d, causal, cus, occ, want):
+    got = _lib.tile_order(Nq, BH, d, causal, Nk=Nk, cus=cus, occ=occ)
+    assert got == expected_order(Nq, Nk, BH, d, causal, cus, occ)
+    assert got == (_lib.FA_FWD_ORDER_PAIRED if want == "paired" else _lib.FA_FWD_ORDER_HEAVY_FIRST)
+    # Strict causal orders like causal; fp16 like bf16.
+    assert _lib.tile_order(Nq, BH, d, "strict" if causal else False, Nk=Nk, cus=cus, occ=occ) == got
+    import torch
+    assert _lib.tile_order(Nq, BH, d, causal, Nk=Nk, dtype=torch.float16, cus=cus, occ=occ) == got
+
+
+def test_tile_order_sweep_matches_rule():
+    for Nq in (128, 256, 1000, 4096, 8192, 12345, 16384):
+        for Nk in (Nq, 2 * Nq, 70000):
+            for BH in (1, 8, 20, 64):
+                for d in (32, 64, 128, 256):
+                    for occ in (1, 2, 3):
+                        got = _lib.tile_order(Nq, BH, d, True, Nk=Nk, cus=256, occ=occ)
+                        assert got == expected_order(Nq, Nk, BH, d, True, 256, occ), \
+                            (Nq, Nk, BH, d, occ)
+
+
+def test_tile_order_argument_errors():
+    lib = _lib.load()
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    bf16, f32 = _lib.FA_DTYPE_BF16, _lib.FA_DTYPE_F32
+    assert lib.fa_fwd_tile_order(0, 128, 1, 128, bf16, 1, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 0, 1, 128, bf16, 1, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 0, 128, bf16, 1, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 0, bf16, 1, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 128, 7, 1, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 128, bf16, 5, 256, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 128, bf16, 1, -1, 2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 128, bf16, 1, 256, -2) == INV
+    assert lib.fa_fwd_tile_order(128, 128, 1, 128, f32, 1, 256, 2) == UNS
