@@ -60,7 +60,7 @@ KERNEL_SOURCES = [
     for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")
 ]
 FWD_KERNEL_TAG = "fwd_kernel"  # in the forward kernel's name, mangled or not
-BWD_KERNEL_TAG = "bwd_"        # in the backward kernels' names (prep, dK/dV, dQ)
+BWD_KERNEL_TAG = "bwd_"        # in the backward kernels' names (dQ, dK/dV)
 
 
 def kernel_source_hash() -> str:
@@ -223,7 +223,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
         last_fwd = max(i for i, n, _ in rows if FWD_KERNEL_TAG in n)
         naive = sum(v for i, n, v in rows if i > last_fwd and BWD_KERNEL_TAG not in n) * 1024.0 * scale
         out["naive_" + key + "_bytes"] = naive
-        # one fa_bwd call (prep + dK/dV + dQ) on the workload, after the naive forward
+        # one fa_bwd call (dQ + dK/dV) on the workload, after the naive forward
         out["bwd_" + key + "_bytes"] = sum(v for _, n, v in rows if BWD_KERNEL_TAG in n) * 1024.0 * scale
         wl = sorted(fwd[:3])[1]
         out[key + "_kib_raw"] = wl
@@ -264,7 +264,7 @@ def summarize_trace(trace_dir: str, bench_file: str, command: str) -> int:
         print("expected one kernel_stats.csv and one kernel_trace.csv", file=sys.stderr)
         return 1
     names = {"fwd_kernel": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
-             "bwd_prep": "bwd_prep_kernel", "mfma_peak": "mfma_peak_kernel"}
+             "mfma_peak": "mfma_peak_kernel"}
     rows = []
     for r in csv.DictReader(open(stats_f[0])):
         if any(t in r["Name"] for t in names):
@@ -736,6 +736,11 @@ def main() -> int:
             bwd_once()
         torch.cuda.synchronize()
         nb = max(5, args.steps // 2)
+        # As for the forward: the calls right after the warm-up (reported),
+        # then backward calls back to back for the settle time, then the
+        # timed calls.
+        ms_bwd_cold = timed_region(bwd_once, nb, stream)
+        bwd_settle = settle_clock(bwd_once, args.settle_ms, stream, group=5)
         t_start.record(stream)
         for _ in range(nb):
             bwd_once()
@@ -751,7 +756,11 @@ def main() -> int:
         ms_fb = t_start.elapsed_time(t_end) / nb
         bflops = W.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
         out["bwd"] = {"ms": round(ms_bwd, 5), "tflops": round(bflops / (ms_bwd * 1e-3) / 1e12, 2),
-                      "flop_convention": "10*B*H*N^2*d, halved for causal"}
+                      "flop_convention": "10*B*H*N^2*d, halved for causal",
+                      "calls": nb,
+                      "cold_start": {"ms": round(ms_bwd_cold, 5),
+                                     "tflops": round(bflops / (ms_bwd_cold * 1e-3) / 1e12, 2)},
+                      "settle": bwd_settle}
         out["fwd_bwd_step"] = {"ms": round(ms_fb, 5),
                                "tflops": round((flops + bflops) / (ms_fb * 1e-3) / 1e12, 2)}
 

@@ -7,15 +7,16 @@
 //   P = exp(S - lse) (0 where hidden or lse = -inf),  D_i = sum_c dO_ic O_ic,
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
 //   dK = scale dS^T Q.
-// Three kernels, no atomics:
-//   prep   D_i and lse_i*log2(e) (+inf for an empty row, so that P = 0) for
-//          every row, into the caller's workspace;
-//   dq     one workgroup per 128 query rows streams the visible key blocks
-//          (64 keys, 32 at D = 256): S^T = K Q^T, dP^T = V dO^T, dS^T,
-//          dQ^T += K^T dS^T (the forward's transposed layout: one query per
-//          lane pair);
+// Two kernels, no atomics, in this order:
+//   dq     one workgroup per 128 query rows first forms D_i and
+//          lse_i*log2(e) (+inf for an empty row, so that P = 0) for its rows
+//          and stores them in the caller's workspace, then streams the
+//          visible key blocks (64 keys, 32 at D = 256): S^T = K Q^T,
+//          dP^T = V dO^T, dS^T, dQ^T += K^T dS^T (the forward's transposed
+//          layout: one query per lane pair);
 //   dkdv   one workgroup per 128 keys streams the blocks of 32 queries that
-//          see them: S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
+//          see them, with their D and lse*log2(e) from the workspace:
+//          S = Q K^T, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS
 //          (one key per lane pair).
 // Streamed blocks go from HBM to LDS with direct 16-byte loads into a double
 // buffer, stored once, row-major. The same copy is read two ways: as rows
@@ -84,39 +85,6 @@ __device__ __forceinline__ int tchunk(int row, int s) {
 // of 8, keeps to a fixed set of heads (shared L2).
 __device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
 __device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
-
-// ---- per row: D_i = sum_c dO_ic O_ic and lse_i * log2(e) ----
-template <int D>
-constexpr int prep_threads_per_row() {  // 8 elements per thread, a power of two threads
-  return D / 8 <= 4 ? 4 : D / 8 <= 8 ? 8 : D / 8 <= 16 ? 16 : 32;
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  typedef Elem<T> E;
-  constexpr int TPR = prep_threads_per_row<D>();  // threads per row (the last ones idle at D = 96)
-  constexpr int RPB = 256 / TPR;
-  const long long rows = (long long)p.B * p.H * p.N;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < rows && c < D / 8) {
-    const u32x4 a = *(const u32x4*)((const T*)p.o + row * D + c * 8);
-    const u32x4 g = *(const u32x4*)((const T*)p.dout + row * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(E::lo(a[e]), E::lo(g[e]), acc);
-      acc = fmaf(E::hi(a[e]), E::hi(g[e]), acc);
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) {
-    p.delta[row] = acc;
-    const float l = p.lse[row];
-    p.lse2[row] = (l == NEG_INF) ? POS_INF : l * LOG2E;  // empty row: P = 0
-  }
-}
 
 // DMA of rows [r0, r0 + ROWS) of two row-major [N, D] 16-bit matrices X0, X1
 // into LDS tiles dst0, dst1 (rows past N repeat row N-1; they are masked by
@@ -264,18 +232,32 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   const T* K = (const T*)p.k + kvhead;
   const T* V = (const T*)p.v + kvhead;
   const T* dO = (const T*)p.dout + head;
+  const T* O = (const T*)p.o + head;
 
   const int qa = q0 + wave * 32;
   const int qrow = qa + n;
   const int qrow_c = min(qrow, N - 1);
   x8 qf[DC], of[DC];
+  float dpart = 0.f;  // this lane's half of D_i = sum_c dO_ic O_ic
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
     qf[c] = *(const x8*)(Q + (size_t)qrow_c * D + 16 * c + 8 * h);
     of[c] = *(const x8*)(dO + (size_t)qrow_c * D + 16 * c + 8 * h);
+    const u32x4 a = __builtin_bit_cast(u32x4, *(const x8*)(O + (size_t)qrow_c * D + 16 * c + 8 * h));
+    const u32x4 g = __builtin_bit_cast(u32x4, of[c]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart = fmaf(E::lo(a[e]), E::lo(g[e]), dpart);
+      dpart = fmaf(E::hi(a[e]), E::hi(g[e]), dpart);
+    }
   }
-  const float lse2 = p.lse2[(size_t)bh * N + qrow_c];
-  const float dl = p.delta[(size_t)bh * N + qrow_c];
+  const float dl = dpart + __shfl_xor(dpart, 32);  // lanes n and n + 32 hold the two halves
+  const float lse_row = p.lse[(size_t)bh * N + qrow_c];
+  const float lse2 = (lse_row == NEG_INF) ? POS_INF : lse_row * LOG2E;  // empty row: P = 0
+  if (h == 0 && qrow < N) {  // for the dK/dV kernel, which runs next
+    p.delta[(size_t)bh * N + qrow] = dl;
+    p.lse2[(size_t)bh * N + qrow] = lse2;
+  }
   __builtin_amdgcn_sched_barrier(0);
   const float scl = p.scale_log2;
   const TileOffsets<D> off(lane);
@@ -603,6 +585,8 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
 template <typename T, int D, bool CAUSAL>
 void launch_grads(const BwdParams& p, long long g1, long long g2, hipStream_t stream) {
   const dim3 blk(NWB * 64);
+  // dQ first: it stores the per-row D and lse*log2(e) the dK/dV kernel reads.
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g1), blk, 0, stream, p);
   if constexpr (D == 256) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DKDV_V>), dim3((unsigned)g2), blk, 0, stream,
                        p);
@@ -612,18 +596,13 @@ void launch_grads(const BwdParams& p, long long g1, long long g2, hipStream_t st
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, DKDV_V | DKDV_K>), dim3((unsigned)g2), blk, 0,
                        stream, p);
   }
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)g1), blk, 0, stream, p);
 }
 
 template <typename T, int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.H * p.N;
-  const long long rpb = 256 / prep_threads_per_row<D>();
-  const long long g0 = (rows + rpb - 1) / rpb;
   const long long g1 = (long long)p.B * p.H * ((p.N + BT - 1) / BT);     // dQ: query tiles
   const long long g2 = (long long)p.B * p.Hkv * ((p.Nk + BT - 1) / BT);  // dK, dV: key tiles
-  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)g0), dim3(256), 0, stream, p);
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.causal)
     launch_grads<T, D, true>(p, g1, g2, stream);
   else

@@ -36,15 +36,15 @@ def _write_counter_csv(path, counter, rows):
 def _profile_dispatches(copy_kib, fwd_kib, sweep_kib, naive_kib, bwd_kib=()):
     # the dispatch order of --profile-run: a fill, three copies, three
     # workload forwards, one forward per sweep N, the naive kernels, then the
-    # backward's prep, dK/dV and dQ kernels
+    # backward's dQ and dK/dV kernels
     fwd = "_ZN2fa12_GLOBAL__N_110fwd_kernelIDF16bLi128ELi64ELb1EEEvNS_9FwdParamsENS_7FwdPlanE"
     rows = [("fill_kernel", 1.0)]
     rows += [("copy_kernel", copy_kib)] * 3
     rows += [(fwd, v) for v in fwd_kib]
     rows += [(fwd, v) for v in sweep_kib]
     rows += [("gemm", v) for v in naive_kib]
-    bwd = ("bwd_prep_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
-    rows += [("_ZN2fa12_GLOBAL__N_1" + bwd[i % 3], v) for i, v in enumerate(bwd_kib)]
+    bwd = ("bwd_dq_kernel", "bwd_dkdv_kernel")
+    rows += [("_ZN2fa12_GLOBAL__N_1" + bwd[i % 2], v) for i, v in enumerate(bwd_kib)]
     return rows
 
 
@@ -55,9 +55,9 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     # FETCH_SIZE reads half the bytes (scale 2), WRITE_SIZE all of them (scale 1)
     fetch_rows = _profile_dispatches(copy / 2, [60000.0, 61000.0, 70000.0],
                                      [100.0, 200.0, 300.0, 400.0, 500.0], [1000.0, 2000.0],
-                                     [7.0, 80000.0, 90000.0])
+                                     [80007.0, 90000.0])
     write_rows = _profile_dispatches(copy, [30000.0, 30000.0, 30000.0],
-                                     [10.0, 20.0, 30.0, 40.0, 50.0], [500.0], [1.0, 2.0, 3.0])
+                                     [10.0, 20.0, 30.0, 40.0, 50.0], [500.0], [3.0, 3.0])
     _write_counter_csv(str(tmp_path / "f" / "vm" / "1_counter_collection.csv"), "FETCH_SIZE",
                        fetch_rows)
     _write_counter_csv(str(tmp_path / "w" / "vm" / "1_counter_collection.csv"), "WRITE_SIZE",
