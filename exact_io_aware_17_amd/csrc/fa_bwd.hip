@@ -354,6 +354,15 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) acc[dt] = E::mfma(tr_operand<x8, D>(ks, off, dt, kc), df[kc], acc[dt]);
+    {
+      // Transposed operand reads (two per product) two products ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < DT * KC; ++i) {
+        if (i + 2 < DT * KC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   issue(0, std::integral_constant<int, 0>());
@@ -483,8 +492,96 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
     const char* os = ST == 0 ? obuf0 : obuf1;
     const float* st = ST == 0 ? stat0 : stat1;
 
-    // Phases in order, each value dead as soon as it is consumed: S, P, dV^T
-    // (needs P), dP, dS (needs P and dP), dK^T.
+    if constexpr (OUT == (DKDV_V | DKDV_K)) {
+      // Both gradients: the two products that need only the streamed rows
+      // (S and dP) first, then P and dS on the VALU, then the two products
+      // that need them (dV^T and dK^T). Two matrix phases per block, so the
+      // other wave of the SIMD has long stretches of matrix work to overlap
+      // with this wave's exponentials.
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 s, dp;
+      zero(s);
+      zero(dp);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        x8 kc;
+        if constexpr (KF_LDS)
+          kc = *(const x8*)(kfl + (wave * DC + c) * 1024 + lane * 16);
+        else
+          kc = kf[c];
+        s = E::mfma(*(const x8*)(qs + off.roff[c]), kc, s);
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) dp = E::mfma(*(const x8*)(os + off.roff[c]), vf[c], dp);
+      {
+        // Operand reads two products ahead: an S product reads a Q row chunk
+        // (and, from LDS, its K fragment), a dP product a dO row chunk.
+        constexpr int RS = KF_LDS ? 2 : 1;  // reads per S product
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * RS, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * DC; ++i) {
+          const int nxt = i + 2;  // the product whose operands are read now
+          const int r = nxt < DC ? RS : (nxt < 2 * DC ? 1 : 0);
+          if (r == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (r == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const bool need_mask = (kw0 + 31 >= kvlen) || (qb0 + BS > N) || (CAUSAL && kw0 + 31 > qb0 + shift);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int query = qb0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= kvlen || query >= N || (CAUSAL && key > query + shift)) s[r] = NEG_INF;
+        }
+      }
+      x8 pf[2], df[2];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        u32x4 wp, wd;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * qc + g2;
+          const f32x4 l4 = *(const f32x4*)(st + 8 * g + 4 * h);
+          const f32x4 d4 = *(const f32x4*)(st + 32 + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 4 * g + 2 * e;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], scl, -l4[2 * e]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], scl, -l4[2 * e + 1]));
+            wp[2 * g2 + e] = E::pack(p0, p1);
+            wd[2 * g2 + e] = E::pack(p0 * (dp[r] - d4[2 * e]), p1 * (dp[r + 1] - d4[2 * e + 1]));
+          }
+        }
+        pf[qc] = __builtin_bit_cast(x8, wp);
+        df[qc] = __builtin_bit_cast(x8, wd);
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc)
+          dva[dt] = E::mfma(tr_operand<x8, D>(os, off, dt, qc), pf[qc], dva[dt]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) dka[dt] = E::mfma(tr_operand<x8, D>(qs, off, dt, qc), df[qc], dka[dt]);
+      {
+        // Transposed operand reads (two per product) two products ahead.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DT; ++i) {
+          if (i + 2 < 4 * DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
+    // One gradient per pass (D = 256): phases in order, each value dead as
+    // soon as it is consumed: S, P, dV^T (needs P), dP, dS (needs P and dP),
+    // dK^T.
     __builtin_amdgcn_s_setprio(1);
     f32x16 s;
     zero(s);
