@@ -365,6 +365,50 @@ def summarize_counters(dirs, workload: int) -> int:
     return 0
 
 
+def summarize_bwd_counters(dirs) -> int:
+    """Counters of the backward's kernels from the fa_bwd call that ends a
+    --profile-run (one dispatch each of the dQ and dK/dV kernels), summed
+    over the --pmc output directories `dirs`, with per-MFMA and share-of-time
+    readings (JSON)."""
+    import csv
+    import glob
+
+    per = {}  # kernel short name -> counter -> value (its last dispatch)
+    for d in dirs:
+        rows = {}  # short name -> dispatch id -> counter -> summed value
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                short = next((t for t in ("bwd_dkdv", "bwd_dq") if t in r["Kernel_Name"]), None)
+                if short is None:
+                    continue
+                c = rows.setdefault(short, {}).setdefault(int(r["Dispatch_Id"]), {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for short, by_id in rows.items():
+            per.setdefault(short, {}).update(by_id[max(by_id)])
+    out = {}
+    for short, v in sorted(per.items()):
+        o = {"counters": v}
+        m = v.get("SQ_INSTS_MFMA")
+        if m:
+            o["per_mfma"] = {k: round(x, 3) for k, x in (
+                ("valu_other_than_mfma", (v["SQ_INSTS_VALU"] - m) / m if "SQ_INSTS_VALU" in v else None),
+                ("exp2", v["SQ_INSTS_VALU_TRANS_F32"] / m if "SQ_INSTS_VALU_TRANS_F32" in v else None),
+                ("lds", v["SQ_INSTS_LDS"] / m if "SQ_INSTS_LDS" in v else None)) if x is not None}
+        if "SQ_WAVE_CYCLES" in v:
+            o["share_of_wave_time"] = {k: round(v[k] / v["SQ_WAVE_CYCLES"], 3)
+                                       for k in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY",
+                                                 "SQ_WAIT_INST_LDS") if k in v}
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in v and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            o["valu_coissued_share_of_mfma_busy"] = round(
+                v["SQ_VALU_MFMA_COEXEC_CYCLES"] / v["SQ_VALU_MFMA_BUSY_CYCLES"], 3)
+        out[short] = o
+    if not out:
+        print("no backward dispatches in " + " ".join(dirs), file=sys.stderr)
+        return 1
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def naive_forward(q, k, v, scale, causal):
     """The unfused path the pages contrast with: S = scale Q K^T and
     P = softmax(S) written to and read back from device memory (bf16), then
@@ -587,9 +631,14 @@ def main() -> int:
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
                     help="median SQ counters of the workload's forward in rocprofv3 --pmc runs "
                          "of --profile-run (one directory per counter pass)")
+    ap.add_argument("--summarize-bwd-counters", nargs="+", metavar="PMC_DIR",
+                    help="SQ counters of the backward kernels of the fa_bwd call that ends "
+                         "--profile-run, in rocprofv3 --pmc runs (one directory per pass)")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.workload)
+    if args.summarize_bwd_counters:
+        return summarize_bwd_counters(args.summarize_bwd_counters)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.traffic_command)
     if args.summarize_trace:

@@ -183,6 +183,37 @@ def test_counter_summary_medians_and_per_block_readings(tmp_path, capsys):
     assert out["per_wave_and_block"]["valu_other_than_mfma"] == pytest.approx(145.7, abs=0.1)
 
 
+def test_bwd_counter_summary_takes_the_last_backward_call(tmp_path, capsys):
+    """Each backward kernel's counters come from its last dispatch (the
+    fa_bwd call that ends --profile-run), summed over rows and passes."""
+    dq = "_ZN2fa12_GLOBAL__N_113bwd_dq_kernelIDF16bLi128ELb1EEEvNS_9BwdParamsE"
+    dkdv = "_ZN2fa12_GLOBAL__N_115bwd_dkdv_kernelIDF16bLi128ELb1ELi3EEEvNS_9BwdParamsE"
+    for pas, counters in (("a", (("SQ_INSTS_MFMA", 1000.0), ("SQ_INSTS_VALU", 4000.0))),
+                          ("b", (("SQ_INSTS_LDS", 2000.0), ("SQ_WAVE_CYCLES", 100.0),
+                                 ("SQ_WAIT_INST_ANY", 25.0)))):
+        rows = []
+        for i, name, mul in ((1, FWD, 1.0), (7, dq, 0.5), (8, dkdv, 0.5), (9, dq, 1.0), (10, dkdv, 2.0)):
+            for c, v in counters:
+                rows += [(i, name, c, v * mul / 2), (i, name, c, v * mul / 2)]
+        d = tmp_path / pas / "vm"
+        d.mkdir(parents=True)
+        with open(d / "1_counter_collection.csv", "w", newline="") as f:
+            wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                               "Counter_Value"])
+            wr.writeheader()
+            for i, n, c, v in rows:
+                wr.writerow({"Dispatch_Id": i, "Kernel_Name": n, "Counter_Name": c,
+                             "Counter_Value": v})
+    assert bench.summarize_bwd_counters([str(tmp_path / "a"), str(tmp_path / "b")]) == 0
+    out = json.loads(capsys.readouterr().out)
+    assert out["bwd_dq"]["counters"]["SQ_INSTS_MFMA"] == 1000.0      # dispatch 9
+    assert out["bwd_dkdv"]["counters"]["SQ_INSTS_MFMA"] == 2000.0    # dispatch 10
+    assert out["bwd_dq"]["per_mfma"]["valu_other_than_mfma"] == pytest.approx(3.0)
+    assert out["bwd_dq"]["per_mfma"]["lds"] == pytest.approx(2.0)
+    assert out["bwd_dkdv"]["share_of_wave_time"]["SQ_WAIT_INST_ANY"] == pytest.approx(0.25)
+    assert bench.summarize_bwd_counters([str(tmp_path / "nothing")]) == 1
+
+
 def test_settle_runs_for_the_requested_time(monkeypatch):
     calls = []
 
