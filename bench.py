@@ -722,6 +722,8 @@ def main() -> int:
 
     flops = W.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms_step * 1e-3) / 1e12
+    paired = (w.dtype != "f32" and bool(w.causal) and
+              fa.tile_order(w.N, w.B * w.H, w.d, w.causal) == fa.FA_FWD_ORDER_PAIRED)
     # One step is one forward launch: the timed region's average launch
     # duration is ms_step.
     achieved = tflops
@@ -755,7 +757,7 @@ def main() -> int:
             "traffic": traffic,
             "kernel": (f"fwd_f32_kernel<{w.d}, {'true' if w.causal else 'false'}>" if f32 else
                        f"fwd_kernel<__bf16, {w.d}, {fa.block_keys(w.B, w.H, w.N, w.d, w.causal)}, "
-                       f"{'true' if w.causal else 'false'}>"),
+                       f"{'true' if w.causal else 'false'}, {'true' if paired else 'false'}>"),
             "flops_per_launch": flops,
             "kernel_ms_mean": round(ms_step, 5),
             "algorithmic_hbm_bytes": W.fwd_bytes(w.B, w.H, w.N, w.d, 2),
