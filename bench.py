@@ -562,7 +562,7 @@ def mfma_probe(dev, stream, flops_target, reps, warmup=3):
 
 def decode_shapes(dev, stream):
     """Decode on a batch of sequences and on one long sequence (few K/V heads
-    over a 131k-token cache, where a tile's key range is split in up to 16
+    over a 131k-token cache, where a tile's key range is split in up to 64
     parts)."""
     return {"batch": decode_comparison(dev, stream),
             "one_long_sequence": decode_comparison(dev, stream, B=1, Nk=131072)}

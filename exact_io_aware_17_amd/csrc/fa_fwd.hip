@@ -57,7 +57,8 @@
 //    about ntiles+1 tiles' worth of blocks, and the pairs of a head read the
 //    same two blocks at a time, so K and V are fetched about once per XCD.
 //  * Load balance: a host plan may cut a tile's key range into up to 16
-//    parts processed by different workgroups. Each part stores its partial
+//    parts (64 when the query rows are a single tile) processed by
+//    different workgroups. Each part stores its partial
 //    state (unnormalised O, reference max, both sums; fp32) and counts its
 //    arrival on the tile's counter; the last part to arrive merges all parts
 //    in part order with the exact block merge ("Exercises", the block
@@ -189,10 +190,10 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     const int rank = blockIdx.x / BH;
     if (plan.nitems > 0) {
       const unsigned it = plan.item[rank];
-      tile0 = (int)(it & 0xfffu);
-      part = (int)((it >> 12) & 15u);
-      nparts = (int)((it >> 16) & 15u) + 1;
-      slot_base = (int)(it >> 20);
+      tile0 = (int)(it & 0x1ffu);
+      part = (int)((it >> 9) & 63u);
+      nparts = (int)((it >> 15) & 63u) + 1;
+      slot_base = (int)(it >> 21);
     } else {
       tile0 = CAUSAL ? ntiles - 1 - rank : rank;  // causal: the latest rows see the most keys
     }
@@ -558,6 +559,67 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
       __syncthreads();
       if (s_arrival != nparts - 1) return;  // another part will merge
       if (tid == 0) atomicExch(ctr, 0);     // ready for the next call
+      if (N - q0 <= 32) {
+        // Only wave 0 holds rows (a packed decode tile, a short last tile):
+        // every wave merges a share of its d tiles (dt = wave, wave + NW,
+        // ...), reading wave 0's slots, and writes those columns of its
+        // rows. The part loops are unrolled so that the loads of several
+        // parts are in flight at once (each costs a memory latency).
+        // No barrier follows.
+        constexpr int DTW = (DT + NW - 1) / NW;  // d tiles per wave
+        if (wave >= DT) return;
+        const int vm0 = lane * 16;
+        float m_all = NEG_INF;
+#pragma unroll 8
+        for (int q = 0; q < nparts; ++q) m_all = fmaxf(m_all, load_coherent16(rm, q * SLOT_ML + vm0)[0]);
+        float l_sum = 0.f, lbf_sum = 0.f;
+        f32x16 mo[DTW];
+#pragma unroll
+        for (int i = 0; i < DTW; ++i) zero(mo[i]);
+#pragma unroll 4
+        for (int q = 0; q < nparts; ++q) {
+          const f32x4 stat = load_coherent16(rm, q * SLOT_ML + vm0);
+          const float c = (stat[0] == NEG_INF) ? 0.f : __builtin_amdgcn_exp2f(stat[0] - m_all);
+          l_sum = fmaf(c, stat[1], l_sum);
+          lbf_sum = fmaf(c, stat[2], lbf_sum);
+#pragma unroll
+          for (int i = 0; i < DTW; ++i) {
+            const int dt = wave + NW * i;
+            if (dt < DT) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const f32x4 v = load_coherent16(ro, q * SLOT_O + (lane + (dt * 4 + g) * 64) * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mo[i][4 * g + e] = fmaf(c, v[e], mo[i][4 * g + e]);
+              }
+            }
+          }
+        }
+        const float l_tot = pair_sum(l_sum);
+        const float l_o = pair_sum(lbf_sum);
+        const bool empty = (l_tot == 0.f);
+        const float inv = empty ? 0.f : 1.f / l_o;
+        const int orow = q0 + n;  // wave 0's row in this lane
+        if (orow < N) {
+          T* O = (T*)p.o + head + (size_t)orow * D;
+#pragma unroll
+          for (int i = 0; i < DTW; ++i) {
+            const int dt = wave + NW * i;
+            if (dt < DT) {
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = E::pack(mo[i][4 * g] * inv, mo[i][4 * g + 1] * inv);
+                w[1] = E::pack(mo[i][4 * g + 2] * inv, mo[i][4 * g + 3] * inv);
+                *(u32x2*)(O + dt * 32 + 8 * g + 4 * h) = w;
+              }
+            }
+          }
+          if (wave == 0 && h == 0 && p.lse)
+            p.lse[(size_t)bh * N + orow] = empty ? NEG_INF : (m_all + log2f(l_tot)) * LN2;
+        }
+        return;
+      }
       if (!live) return;                    // no barrier follows
 
       // Every part, this one included, is read back and combined in part
@@ -565,6 +627,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
       // The row statistics are read twice (max first, then the sums), so any
       // number of parts merges in the same registers.
       float m_all = NEG_INF;
+#pragma unroll 8
       for (int q = 0; q < nparts; ++q) m_all = fmaxf(m_all, load_coherent16(rm, q * SLOT_ML + vm)[0]);
       float l_sum = 0.f, lbf_sum = 0.f;
 #pragma unroll

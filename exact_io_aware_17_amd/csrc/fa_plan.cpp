@@ -6,10 +6,11 @@
 // causal mask the tiles of late query rows stream up to N/BN blocks and early
 // ones a few, and without it N/BM tiles of equal cost may fill the resident
 // slots unevenly; either way the last workgroups can leave most of the chip
-// idle. The planner splits the heaviest tiles into up to sixteen contiguous key
-// ranges (the block merge of the online softmax, "Exercises" of the
-// interactive explainer "The Flash Attention", combines their partial states
-// exactly), orders all items longest first, and keeps the split threshold
+// idle. The planner splits the heaviest tiles into up to sixteen contiguous
+// key ranges (up to 64 for a single query tile; the block merge of the online
+// softmax, "Exercises" of the interactive explainer "The Flash Attention",
+// combines their partial states exactly), orders all items longest first,
+// and keeps the split threshold
 // whose simulated schedule finishes earliest. The simulation follows each
 // compute unit: it holds up to `occ` workgroups, its throughput depends on
 // how many are resident (a lone workgroup keeps a compute unit well under
@@ -55,6 +56,10 @@ namespace {
 // slower.
 constexpr double kItemCost = 2.0;
 constexpr double kSplitCost = 7.0;
+// The last part of a split tile to arrive reads every part's partial state:
+// kSplitCost covers up to FWD_MAX_PARTS parts, and each part beyond them adds
+// about this much.
+constexpr double kMergePerPart = 0.15;
 // A split plan is used only if it shortens the simulated schedule this much.
 // On grids of several waves of workgroups the simulation still promises
 // 7-20% where the device gains nothing, so only a clearly under-filled grid
@@ -129,18 +134,23 @@ double simulate(const std::vector<Item>& items, int BH, int cus, int occ) {
   return end;
 }
 
+int max_parts(int ntiles) { return ntiles == 1 ? FWD_MAX_PARTS_ONE_TILE : FWD_MAX_PARTS; }
+
 // Items for split threshold T (blocks): tiles above T are cut into
-// min(FWD_MAX_PARTS, ceil(nb / T)) parts. T <= 0 means no split.
+// min(max_parts, ceil(nb / T)) parts. T <= 0 means no split.
 std::vector<Item> make_items(int N, int Nk, bool causal, int bn, int T) {
   const int ntiles = (N + FWD_BM - 1) / FWD_BM;
   std::vector<Item> items;
   for (int t = 0; t < ntiles; ++t) {
     const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
     int np = 1;
-    if (T > 0 && nb > T) np = std::min(FWD_MAX_PARTS, (nb + T - 1) / T);
+    if (T > 0 && nb > T) np = std::min(max_parts(ntiles), (nb + T - 1) / T);
     for (int part = 0; part < np; ++part) {
       const int blocks = (part + 1) * nb / np - part * nb / np;
-      items.push_back({t, part, np, blocks + kItemCost + (np > 1 ? kSplitCost : 0.0)});
+      items.push_back({t, part, np,
+                       blocks + kItemCost +
+                           (np > 1 ? kSplitCost + kMergePerPart * std::max(0, np - FWD_MAX_PARTS)
+                                   : 0.0)});
     }
   }
   std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
@@ -164,8 +174,10 @@ std::shared_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
   const double base = simulate(make_items(N, Nk, causal, bn, 0), BH, cus, occ);
   double best = base * kMinGain;
   int bestT = 0;
-  static const double fracs[] = {0.875, 0.75, 0.625, 0.5, 0.4, 1.0 / 3.0, 0.25, 0.125, 0.0625};
+  static const double fracs[] = {0.875, 0.75, 0.625, 0.5, 0.4, 1.0 / 3.0, 0.25, 0.125, 0.0625,
+                                 1.0 / 24, 1.0 / 32, 1.0 / 48, 1.0 / 64};
   for (double f : fracs) {
+    if (ntiles > 1 && f < 0.0625) break;  // at most 16 parts when several tiles split
     const int T = std::max(4, (int)(nbmax * f + 0.999));
     if (T >= nbmax) continue;
     const std::vector<Item> items = make_items(N, Nk, causal, bn, T);
@@ -183,16 +195,16 @@ std::shared_ptr<FwdPlan> build_plan(int N, int Nk, int BH, bool causal, int bn, 
   int nslots = 0;
   for (int t = 0; t < ntiles; ++t) {
     const int nb = fwd_tile_blocks(N, Nk, t, causal, bn);
-    const int np = (nb > bestT) ? std::min(FWD_MAX_PARTS, (nb + bestT - 1) / bestT) : 1;
+    const int np = (nb > bestT) ? std::min(max_parts(ntiles), (nb + bestT - 1) / bestT) : 1;
     base_of[t] = nslots;
     if (np > 1) nslots += np;
   }
-  if (nslots >= (1 << 12)) return plan;
+  if (nslots >= (1 << 11) || ntiles > (1 << 9)) return plan;
   for (size_t i = 0; i < items.size(); ++i) {
     const Item& it = items[i];
     const int sb = (it.nparts > 1) ? base_of[it.tile] : 0;
-    plan->item[i] = (uint32_t)it.tile | ((uint32_t)it.part << 12) | ((uint32_t)(it.nparts - 1) << 16) |
-                    ((uint32_t)sb << 20);
+    plan->item[i] = (uint32_t)it.tile | ((uint32_t)it.part << 9) | ((uint32_t)(it.nparts - 1) << 15) |
+                    ((uint32_t)sb << 21);
   }
   plan->nitems = (int)items.size();
   plan->nslots = nslots;

@@ -75,7 +75,7 @@ struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 #endif
 
-#define FA_ABI_VERSION 9
+#define FA_ABI_VERSION 10
 
 typedef enum {
   FA_OK = 0,
@@ -245,9 +245,10 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
  * compute units and `occ` resident workgroups per compute unit, returns the
  * number of work items (0 = one item per query tile, no split) and copies up
  * to max_items of them to `items`, each
- *   tile | part << 12 | (nparts - 1) << 16 | slot_base << 20
- * (at most 16 parts per tile; plans are made for at most 4096 tiles per head),
- * in dispatch order; *nslots receives the partial-state slots per head.
+ *   tile | part << 9 | (nparts - 1) << 15 | slot_base << 21
+ * (a plan has at most 512 items; a tile is split into at most 16 parts, or
+ * 64 when the query rows are a single tile), in dispatch order; *nslots
+ * receives the partial-state slots per head.
  * Query tiles are 128 rows; a tile's keys stream in blocks of 64 keys;
  * part p of n covers blocks [p * nb / n, (p + 1) * nb / n) of the tile's nb
  * blocks.

@@ -27,6 +27,7 @@ def block_keys(d, Nq, Nk, BH, causal, cus):
     """Keys per block of the forward launch (the header's rule: 64 keys)."""
     return 64
 ITEM, SPLIT = 2.0, 7.0   # cost per item and extra per split part, in key blocks
+MERGE = 0.15             # extra per split part for each part of its tile beyond 16 (the merge)
 MIN_GAIN = 0.75
 
 
@@ -37,7 +38,8 @@ def tile_blocks(N, t, causal, Nk=None, bn=32):
 
 
 def decode(item):
-    return item & 0xFFF, (item >> 12) & 15, ((item >> 16) & 15) + 1, item >> 20
+    """tile | part << 9 | (nparts - 1) << 15 | slot_base << 21 (the header's layout)."""
+    return item & 0x1FF, (item >> 9) & 63, ((item >> 15) & 63) + 1, item >> 21
 
 
 def cu_throughput(k, occ):
@@ -113,7 +115,8 @@ def _costs(items, N, Nk, causal, bn):
     for it in items:
         t, part, np_, _ = decode(it)
         nb = tile_blocks(N, t, causal, Nk, bn)
-        out.append((part + 1) * nb // np_ - part * nb // np_ + ITEM + (SPLIT if np_ > 1 else 0))
+        out.append((part + 1) * nb // np_ - part * nb // np_ + ITEM
+                   + (SPLIT + MERGE * max(0, np_ - 16) if np_ > 1 else 0))
     return out
 
 
@@ -172,11 +175,16 @@ def test_split_only_underfilled_grids():
     assert _lib.schedule(16384, 2, True, 256, 3) == (items, nslots)  # cached, deterministic
     assert max(decode(it)[2] for it in _lib.schedule(1024, 1, False, 256, 3)[0]) == 4
     # Decode (one query per head) over a long cache: every head's only tile
-    # split, here into the most parts an item can have.
-    items, nslots = _lib.schedule(1, 32, True, 256, 3, 32768)
-    assert len(items) == 16 and nslots == 16
-    assert sorted(decode(it)[1] for it in items) == list(range(16))
-    assert all(decode(it)[2] == 16 and decode(it)[3] == 0 for it in items)
+    # split, into more parts than a multi-tile plan may use (at most 64).
+    for BH, Nk in ((32, 32768), (8, 131072), (8, 32768)):
+        items, nslots = _lib.schedule(1, BH, True, 256, 3, Nk)
+        P = len(items)
+        assert 16 < P <= 64 and nslots == P
+        assert sorted(decode(it)[1] for it in items) == list(range(P))
+        assert all(decode(it)[0] == 0 and decode(it)[2] == P and decode(it)[3] == 0 for it in items)
+    # Several tiles: never more than 16 parts per tile.
+    for args in ((16384, 2, True, 256, 3), (1024, 1, False, 256, 3), (2048, 1, True, 256, 2, 65536)):
+        assert max(decode(it)[2] for it in _lib.schedule(*args)[0]) <= 16
     assert _lib.schedule(1, 32, True, 256, 3, 32768) != _lib.schedule(1, 32, True, 256, 3, 1)
 
 

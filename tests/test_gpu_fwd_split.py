@@ -107,3 +107,93 @@ def test_short_workspace_runs_unsplit():
 def test_metric_shape_is_not_split():
     # Several waves of workgroups: the plan keeps one workgroup per tile.
     assert fa.split_workspace_bytes(2, 16, 4096, 128, True) == 0
+
+
+# Decode over long caches: one query per head, grouped K/V heads packed as the
+# rows of a single query tile, whose key range is cut into more than 16 parts
+# (up to 64); the last part to arrive merges with all four waves, each taking
+# a share of the d columns of the one wave that holds rows.
+# (B, H, Hkv, Nk, d, dtype, causal, kv_lens)
+DECODE = [
+    (1, 32, 8, 131072, 128, torch.bfloat16, True, None),
+    (1, 8, 8, 32768, 64, torch.bfloat16, True, None),         # d = 64: two waves merge
+    (1, 16, 4, 32768, 256, torch.bfloat16, True, None),       # d = 256: two d tiles per wave
+    (1, 8, 2, 32768, 32, torch.bfloat16, False, None),        # d = 32: one wave merges
+    (1, 12, 4, 40000, 96, torch.float16, True, None),         # d = 96, fp16, ragged last block
+    (2, 8, 2, 65536, 128, torch.bfloat16, True, [65536, 0]),  # an empty sequence
+    (1, 4, 4, 50000, 128, torch.bfloat16, "strict", [30001]),  # unpacked: one row per head
+]
+
+
+def _decode_ids(c):
+    B, H, Hkv, Nk, d, dt, causal, kv = c
+    tag = {False: "", True: "c", "strict": "s"}[causal]
+    return f"B{B}H{H}g{Hkv}k{Nk}d{d}{'f16' if dt == torch.float16 else ''}{tag}{'' if kv is None else 'kv'}"
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[_decode_ids(c) for c in DECODE])
+def test_decode_with_many_parts_matches_oracle(case):
+    B, H, Hkv, Nk, d, dtype, causal, kvl = case
+    say(f"case decode B={B} H={H} Hkv={Hkv} Nk={Nk} d={d} {dtype} causal={causal} kv_lens={kvl}")
+    g = torch.Generator().manual_seed(1900 + Nk + d)
+    q = torch.randn(B, H, 1, d, generator=g).to(dtype)
+    k = torch.randn(B, Hkv, Nk, d, generator=g).to(dtype)
+    v = torch.randn(B, Hkv, Nk, d, generator=g).to(dtype)
+    kv = None if kvl is None else torch.tensor(kvl, dtype=torch.int32)
+    need = fa.split_workspace_bytes(B, H, 1, d, causal, Hkv, Nk, dtype)
+    assert need > 0, "the plan was expected to split this shape"
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    scale = fa.default_scale(d)
+    o, lse = fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale,
+                    kv_lens=None if kv is None else kv.to(DEV), split=True, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_fwd(q, k, v, scale, causal, kv)
+    tol = (BF16_O_MAX, BF16_O_MEAN) if dtype == torch.bfloat16 else (5e-3, 5e-4)
+    check_o(to64(o), o_ref, *tol)
+    check_lse(to64(lse), lse_ref, BF16_LSE_ABS, BF16_LSE_REL)
+    assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0
+    if kvl is not None and 0 in kvl:
+        b0 = kvl.index(0)
+        assert torch.all(o[b0] == 0).item() and torch.all(torch.isneginf(lse[b0])).item()
+
+
+def test_decode_plans_use_more_than_sixteen_parts():
+    """The decode shapes above take plans of more than 16 parts at any
+    occupancy from 1 to 4 workgroups per compute unit, so that the many-part
+    merge is what their parity cases check. Launch shape: B * Hkv heads of
+    H / Hkv rows when grouped heads are packed; the strict mask and H = Hkv
+    keep one row per head."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, H, Hkv, Nk, d, _, causal, _ in DECODE:
+        packed = H != Hkv and causal != "strict"
+        rows, heads = (H // Hkv, B * Hkv) if packed else (1, B * H)
+        for occ in (1, 2, 3, 4):
+            items, nslots = fa.schedule(rows, heads, causal, cus, occ, Nk=Nk, d=d)
+            assert len(items) > 16 and nslots == len(items), (B, H, Hkv, Nk, d, occ, len(items))
+
+
+@pytest.mark.parametrize("Nq", [40, 100])
+def test_short_query_chunk_with_many_parts(Nq):
+    """A chunk of Nq < 128 queries after a long cache: one query tile per head
+    split into more than 16 parts, with rows in two (Nq = 40) or four waves
+    (Nq = 100), so the last part merges each wave's own rows."""
+    B, H, Nk, d = 1, 4, 40000, 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for occ in (1, 2, 3, 4):
+        assert len(fa.schedule(Nq, B * H, True, cus, occ, Nk=Nk, d=d)[0]) > 16
+    say(f"case chunk B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
+    g = torch.Generator().manual_seed(1950 + Nq)
+    q = torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    need = fa.split_workspace_bytes(B, H, Nq, d, True, H, Nk)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    scale = fa.default_scale(d)
+    o, lse = fa.fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale, split=True,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_fwd(q, k, v, scale, True)
+    check_o(to64(o), o_ref, BF16_O_MAX, BF16_O_MEAN)
+    check_lse(to64(lse), lse_ref, BF16_LSE_ABS, BF16_LSE_REL)
+    assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0
