@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     FA_DTYPE_F32,
     FA_ERR_HIP,
     FA_ERR_INVALID_ARG,
+    FA_BWD_DKDV_HEAD_SEQUENTIAL,
+    FA_BWD_DQ_HEAD_SEQUENTIAL,
     FA_ERR_UNSUPPORTED,
     FA_FWD_ORDER_HEAVY_FIRST,
     FA_FWD_ORDER_PAIRED,
@@ -23,6 +25,7 @@ from ._lib import (  # noqa: F401
     FaError,
     block_keys,
     bwd,
+    bwd_tile_order,
     bwd_workspace_bytes,
     default_scale,
     dtype_code,

@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -48,6 +48,7 @@ SIGNATURES = {
                        _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp]),
     "fa_fwd_schedule": (_i, [_i, _i, _i, _i, _i, _i, _i, _vp, _i, _vp]),
     "fa_fwd_tile_order": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "fa_bwd_tile_order": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "fa_fwd_block_keys": (_i, [_i, _i, _i, _i, _i, _i]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_abi_version": (_i, []),
@@ -229,6 +230,22 @@ def tile_order(N: int, BH: int, d: int, causal, Nk: Optional[int] = None,
                                      mask_kind(causal), cus, occ))
     if n < 0:
         raise FaError("fa_fwd_tile_order", n, status_string(n))
+    return n
+
+
+FA_BWD_DQ_HEAD_SEQUENTIAL = 1
+FA_BWD_DKDV_HEAD_SEQUENTIAL = 2
+
+
+def bwd_tile_order(B: int, H: int, N: int, d: int, Hkv: Optional[int] = None,
+                   Nk: Optional[int] = None, cus: int = 0, occ: int = 0) -> int:
+    """fa_bwd_tile_order: which gradient kernels run each XCD's heads one after
+    another (FA_BWD_*_HEAD_SEQUENTIAL bits) for N query rows over Nk keys
+    (default N) and Hkv K/V heads (default H)."""
+    n = int(load().fa_bwd_tile_order(B, H, H if Hkv is None else Hkv, N, N if Nk is None else Nk,
+                                     d, cus, occ))
+    if n < 0:
+        raise FaError("fa_bwd_tile_order", n, status_string(n))
     return n
 
 

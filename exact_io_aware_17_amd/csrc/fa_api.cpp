@@ -180,6 +180,21 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Resident workgroups per compute unit of both gradient kernels (their
+// launch bounds: two, one at d = 256).
+int bwd_occupancy(int d) { return d == 256 ? 1 : 2; }
+
+// Work order of the two gradient kernels (bwd_head_sequential per kernel).
+void bwd_orders(int B, int H, int Hkv, int Nq, int Nk, int d, int cus, int occ, int& seq_dq,
+                int& seq_dkdv) {
+  (void)d;
+  const long long bt = fa::BWD_BT;
+  const long long dq_items = (long long)B * H * ((Nq + bt - 1) / bt);
+  const long long dkdv_items = (long long)B * Hkv * ((Nk + bt - 1) / bt);
+  seq_dq = ((B * H) % 8 == 0 && fa::bwd_head_sequential(dq_items, cus, occ)) ? 1 : 0;
+  seq_dkdv = ((B * Hkv) % 8 == 0 && fa::bwd_head_sequential(dkdv_items, cus, occ)) ? 1 : 0;
+}
+
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H,
                int Hkv, int Nq, int Nk, int d, int dtype, float scale, int mask_kind,
@@ -233,6 +248,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
   p.scale_log2 = scale_log2(scale);
   p.causal = (mask_kind != FA_MASK_NONE);
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
+  bwd_orders(B, H, Hkv, Nq, Nk, d, fa::fwd_device_cus(), bwd_occupancy(d), p.seq_dq, p.seq_dkdv);
   hipError_t e = fa::launch_bwd(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -328,6 +344,19 @@ int fa_fwd_tile_order(int Nq, int Nk, int BH, int d, int dtype, int mask_kind, i
   }
   return fa::fwd_pair_tiles(Nq, Nk, d, BH, causal, cus, occ) ? FA_FWD_ORDER_PAIRED
                                                              : FA_FWD_ORDER_HEAVY_FIRST;
+}
+
+int fa_bwd_tile_order(int B, int H, int Hkv, int Nq, int Nk, int d, int cus, int occ) {
+  if (cus < 0 || occ < 0) return FA_ERR_INVALID_ARG;
+  const int st = check_common(B, H, Hkv, Nq, Nk, d, 1.f, FA_MASK_NONE);
+  if (st != FA_OK) return st;
+  if (cus == 0 && occ == 0) {
+    cus = fa::fwd_device_cus();
+    occ = bwd_occupancy(d);
+  }
+  int seq_dq = 0, seq_dkdv = 0;
+  bwd_orders(B, H, Hkv, Nq, Nk, d, cus, occ, seq_dq, seq_dkdv);
+  return (seq_dq ? FA_BWD_DQ_HEAD_SEQUENTIAL : 0) | (seq_dkdv ? FA_BWD_DKDV_HEAD_SEQUENTIAL : 0);
 }
 
 int fa_fwd_block_keys(int B, int H, int Nq, int Nk, int d, int mask_kind) {

@@ -41,6 +41,7 @@ using namespace dev;
 constexpr int BS = 32;   // streamed query rows per block in dkdv
 constexpr int NWB = 4;   // waves per workgroup
 constexpr int BT = 32 * NWB;  // rows owned by a workgroup (queries in dq, keys in dkdv)
+static_assert(BT == BWD_BT, "workgroup rows match the host's work-order rule");
 
 // Waves per SIMD each kernel's register budget is sized for.
 #ifndef FA_BWD_DQ_OCC
@@ -79,12 +80,21 @@ __device__ __forceinline__ int tchunk(int row, int s) {
 }
 
 
-// Tile-major work order: workgroup id w takes tile rank w / (B*H) of head
-// w % (B*H). Workgroups are dispatched in id order, round-robin over the 8
-// XCDs, so each XCD starts with the heaviest tiles and, when B*H is a multiple
-// of 8, keeps to a fixed set of heads (shared L2).
-__device__ __forceinline__ int tile_rank(int BH) { return blockIdx.x / BH; }
-__device__ __forceinline__ int tile_head(int BH) { return blockIdx.x % BH; }
+// Work order. Workgroups are dispatched in id order, round-robin over the 8
+// XCDs (id % 8). Tile-major (seq = 0): workgroup id w takes tile rank
+// w / (B*H) of head w % (B*H), so each XCD starts with the heaviest tiles
+// and, when B*H is a multiple of 8, keeps to a fixed set of heads (x, x+8,
+// ...). Head-sequential (seq = 1, B*H a multiple of 8): XCD x takes the same
+// heads but runs them one after another, rank-major within a head, so that
+// few heads' streamed operands share its L2 at a time.
+__device__ __forceinline__ int tile_rank(int BH, int nt, int seq) {
+  if (seq && (BH & 7) == 0) return (blockIdx.x >> 3) % nt;
+  return blockIdx.x / BH;
+}
+__device__ __forceinline__ int tile_head(int BH, int nt, int seq) {
+  if (seq && (BH & 7) == 0) return (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) / nt);
+  return blockIdx.x % BH;
+}
 
 // DMA of rows [r0, r0 + ROWS) of two row-major [N, D] 16-bit matrices X0, X1
 // into LDS tiles dst0, dst1 (rows past N repeat row N-1; they are masked by
@@ -213,8 +223,8 @@ __global__ __launch_bounds__(NWB * 64, D == 256 ? 1 : FA_BWD_DQ_OCC) void bwd_dq
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N;
   const int ntiles = (N + BT - 1) / BT;
-  const int bh = tile_head(p.B * p.H);
-  int tile = tile_rank(p.B * p.H);
+  const int bh = tile_head(p.B * p.H, ntiles, p.seq_dq);
+  int tile = tile_rank(p.B * p.H, ntiles, p.seq_dq);
   if (CAUSAL) tile = ntiles - 1 - tile;  // the latest query rows see the most keys
   const int b = bh / p.H;
   const int q0 = tile * BT;
@@ -410,8 +420,9 @@ __global__ __launch_bounds__(NWB * 64, dkdv_waves_per_simd(D)) void bwd_dkdv_ker
   const int n = lane & 31, h = lane >> 5;
   const int N = p.N, Nk = p.Nk;
   const int G = p.H / p.Hkv;  // query heads per K/V head
-  const int bkv = tile_head(p.B * p.Hkv);
-  const int tile = tile_rank(p.B * p.Hkv);  // the earliest keys are seen by the most queries
+  const int ntk = (p.Nk + BT - 1) / BT;
+  const int bkv = tile_head(p.B * p.Hkv, ntk, p.seq_dkdv);
+  const int tile = tile_rank(p.B * p.Hkv, ntk, p.seq_dkdv);  // the earliest keys are seen by the most queries
   const int b = bkv / p.Hkv;
   const int kb0 = tile * BT;
   const int shift = CAUSAL ? Nk - N - p.diag : 0;  // causal: key visible iff key <= query + shift

@@ -41,6 +41,7 @@ struct FwdParams {
 
 // Forward tiling shared by the kernel and the host planner.
 constexpr int FWD_BM = 128;                 // query rows per workgroup
+constexpr int BWD_BT = 128;                 // rows per gradient workgroup (queries in dQ, keys in dK/dV)
 // Keys per streamed block of the 16-bit forward (the planner counts these
 // blocks): 64 at every head dimension and shape.
 constexpr int FWD_BN = 64;
@@ -124,6 +125,10 @@ struct BwdParams {
   float scale_log2;
   int causal;
   int diag;                // as FwdParams
+  // Work order of each gradient kernel (bwd_head_sequential): 0 tile-major
+  // (every XCD starts with the heaviest tiles of all its heads), 1 each XCD
+  // runs its heads one after another.
+  int seq_dq, seq_dkdv;
 };
 
 // Each launcher enqueues on `stream` and returns hipGetLastError().
@@ -133,6 +138,15 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
+// Whether a backward kernel with `items` workgroups (heads a multiple of 8)
+// should run each XCD's heads one after another: when the grid is at least
+// 16 rounds of the cus * occ resident slots. The tile-major order then keeps
+// every head of an XCD streaming its operands at once, past the L2 and the
+// Infinity Cache, while the longest-first balance that the sequential order
+// gives up within an XCD matters little over that many rounds (measured:
+// 2 rounds -13 %, 4 rounds -4 %, 8 rounds -1 to -4 %, 16 rounds +4 to +13 %,
+// 32 rounds +13 to +31 %).
+bool bwd_head_sequential(long long items, int cus, int occ);
 
 // fa_fwd_ex_noalloc's workspace: a device array of this many bytes per GPU
 // (fa_noalloc.hip). noalloc_scratch() returns the current device's copy

@@ -39,6 +39,11 @@ int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn) {
   return (int)((kend + bn - 1) / bn);
 }
 
+bool bwd_head_sequential(long long items, int cus, int occ) {
+  if (cus <= 0 || occ <= 0) return false;
+  return items >= 16ll * cus * occ;
+}
+
 bool fwd_pair_tiles(int N, int Nk, int d, int BH, bool causal, int cus, int occ) {
   const long long ntiles = ((long long)N + FWD_BM - 1) / FWD_BM;
   if (!causal || ntiles < 2 || Nk <= 0 || d <= 0 || BH <= 0 || cus <= 0 || occ <= 0) return false;

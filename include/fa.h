@@ -75,7 +75,7 @@ struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 #endif
 
-#define FA_ABI_VERSION 10
+#define FA_ABI_VERSION 11
 
 typedef enum {
   FA_OK = 0,
@@ -287,6 +287,26 @@ typedef enum {
  * or FA_ERR_UNSUPPORTED for FA_DTYPE_F32.
  */
 int fa_fwd_tile_order(int Nq, int Nk, int BH, int d, int dtype, int mask_kind, int cus, int occ);
+
+/* Work order of the backward's gradient kernels; fa_bwd_tile_order. */
+#define FA_BWD_DQ_HEAD_SEQUENTIAL 1    /* the dQ kernel runs each XCD's heads one after another */
+#define FA_BWD_DKDV_HEAD_SEQUENTIAL 2  /* the dK/dV kernel does */
+
+/*
+ * Host-side view of the work order fa_bwd / fa_bwd_ex use for these sizes
+ * (shapes as fa_bwd_ex) on `cus` compute units with `occ` resident
+ * workgroups per compute unit (cus = occ = 0: the current device's compute
+ * units and the kernels' own occupancy, two workgroups per compute unit, one
+ * at d = 256). Each gradient kernel takes its tiles tile-major (every XCD
+ * starts with the heaviest tiles of all its heads) unless its grid is at
+ * least 16 rounds of the resident slots and its head count (B*H for dQ,
+ * B*Hkv for dK/dV) a multiple of 8; then each XCD runs its heads one after
+ * another, so that few heads' streamed operands share its L2 at a time. The
+ * gradients are bitwise the same either way.
+ * Returns a combination of FA_BWD_DQ_HEAD_SEQUENTIAL and
+ * FA_BWD_DKDV_HEAD_SEQUENTIAL, or FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED.
+ */
+int fa_bwd_tile_order(int B, int H, int Hkv, int Nq, int Nk, int d, int cus, int occ);
 
 /*
  * Keys per streamed block that fa_fwd / fa_fwd_ex use for these sizes on the

@@ -291,3 +291,42 @@ def test_tile_order_argument_errors():
     assert lib.fa_fwd_tile_order(128, 128, 1, 128, bf16, 1, -1, 2) == INV
     assert lib.fa_fwd_tile_order(128, 128, 1, 128, bf16, 1, 256, -2) == INV
     assert lib.fa_fwd_tile_order(128, 128, 1, 128, f32, 1, 256, 2) == UNS
+
+
+# ---- backward work order (fa_bwd_tile_order; host only with explicit cus, occ) ----
+
+def expected_bwd_order(B, H, Hkv, Nq, Nk, cus, occ):
+    """The header's rule, per gradient kernel: head-sequential when its head
+    count is a multiple of 8 and its grid is at least 16 rounds of slots."""
+    dq = (B * H) % 8 == 0 and B * H * -(-Nq // BM) >= 16 * cus * occ
+    dkdv = (B * Hkv) % 8 == 0 and B * Hkv * -(-Nk // BM) >= 16 * cus * occ
+    return (_lib.FA_BWD_DQ_HEAD_SEQUENTIAL if dq else 0) | (_lib.FA_BWD_DKDV_HEAD_SEQUENTIAL if dkdv else 0)
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,occ,want", [
+    (2, 16, 16, 4096, 4096, 128, 2, 0),      # the metric backward: 2 rounds
+    (4, 16, 16, 8192, 8192, 128, 2, 0),      # 8 rounds
+    (8, 32, 32, 4096, 4096, 128, 2, 3),      # 16 rounds
+    (8, 32, 8, 8192, 8192, 128, 2, 1),       # grouped: dK/dV's grid is 4x smaller
+    (3, 20, 20, 16384, 16384, 128, 2, 0),    # 60 heads: not a multiple of 8
+    (8, 32, 16, 4096, 4096, 256, 1, 3),
+    (16, 32, 32, 1024, 65536, 128, 2, 2),    # Nq < Nk: only dK/dV's grid is large
+])
+def test_bwd_tile_order_rule(B, H, Hkv, Nq, Nk, d, occ, want):
+    got = _lib.bwd_tile_order(B, H, Nq, d, Hkv=Hkv, Nk=Nk, cus=256, occ=occ)
+    assert got == want == expected_bwd_order(B, H, Hkv, Nq, Nk, 256, occ)
+
+
+def test_bwd_tile_order_sweep_and_errors():
+    for B in (1, 2, 8, 16):
+        for H, Hkv in ((16, 16), (32, 8), (12, 4)):
+            for N in (128, 1000, 4096, 16384):
+                for occ in (1, 2):
+                    assert _lib.bwd_tile_order(B, H, N, 128, Hkv=Hkv, cus=256, occ=occ) == \
+                        expected_bwd_order(B, H, Hkv, N, N, 256, occ)
+    lib = _lib.load()
+    INV, UNS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_tile_order(0, 1, 1, 128, 128, 128, 256, 2) == INV
+    assert lib.fa_bwd_tile_order(1, 3, 2, 128, 128, 128, 256, 2) == INV   # H % Hkv != 0
+    assert lib.fa_bwd_tile_order(1, 1, 1, 128, 128, 128, -1, 2) == INV
+    assert lib.fa_bwd_tile_order(1, 1, 1, 128, 128, 48, 256, 2) == UNS   # head dimension
