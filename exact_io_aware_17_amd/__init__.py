@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     FA_BWD_DKDV_HEAD_SEQUENTIAL,
     FA_BWD_DQ_HEAD_SEQUENTIAL,
     FA_ERR_UNSUPPORTED,
+    FA_FWD_ORDER_HEAD_SEQUENTIAL,
     FA_FWD_ORDER_HEAVY_FIRST,
     FA_FWD_ORDER_PAIRED,
     FA_MASK_CAUSAL,

@@ -24,7 +24,7 @@ FA_MASK_CAUSAL_STRICT = 2
 FA_DTYPE_BF16 = 0
 FA_DTYPE_F16 = 1
 FA_DTYPE_F32 = 2
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -219,13 +219,15 @@ def schedule(N: int, BH: int, causal, cus: int, occ: int, Nk: Optional[int] = No
 
 FA_FWD_ORDER_HEAVY_FIRST = 0
 FA_FWD_ORDER_PAIRED = 1
+FA_FWD_ORDER_HEAD_SEQUENTIAL = 2
 
 
 def tile_order(N: int, BH: int, d: int, causal, Nk: Optional[int] = None,
                dtype: torch.dtype = torch.bfloat16, cus: int = 0, occ: int = 0) -> int:
-    """fa_fwd_tile_order: FA_FWD_ORDER_HEAVY_FIRST or FA_FWD_ORDER_PAIRED for
-    N query rows against Nk keys (default N); cus = occ = 0 asks for the
-    current device's compute units and occupancy."""
+    """fa_fwd_tile_order: FA_FWD_ORDER_HEAVY_FIRST, FA_FWD_ORDER_PAIRED or
+    FA_FWD_ORDER_HEAD_SEQUENTIAL for N query rows against Nk keys (default N)
+    and BH query heads; cus = occ = 0 asks for the current device's compute
+    units and occupancy."""
     n = int(load().fa_fwd_tile_order(N, N if Nk is None else Nk, BH, d, dtype_code(dtype),
                                      mask_kind(causal), cus, occ))
     if n < 0:

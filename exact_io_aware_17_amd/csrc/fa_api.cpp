@@ -126,6 +126,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   p.causal = (mask_kind != FA_MASK_NONE);
   p.diag = (mask_kind == FA_MASK_CAUSAL_STRICT) ? 1 : 0;
   p.pair = 0;
+  p.seq = 0;
   p.nslots = 0;
   p.counters = nullptr;
   p.part_ml = nullptr;
@@ -176,6 +177,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     }
   }
   if (plan->nitems == 0 && fa::fwd_pair_tiles(Nq, Nk, d, BH, p.causal != 0, cus, occ)) p.pair = 1;
+  if (plan->nitems == 0 && fa::fwd_head_sequential(Nq, Nk, d, BH, p.causal != 0, cus, occ))
+    p.seq = 1;
   hipError_t e = fa::launch_fwd(p, *plan, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -184,15 +187,15 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
 // launch bounds: two, one at d = 256).
 int bwd_occupancy(int d) { return d == 256 ? 1 : 2; }
 
-// Work order of the two gradient kernels (bwd_head_sequential per kernel).
+// Work order of the two gradient kernels (head_sequential per kernel).
 void bwd_orders(int B, int H, int Hkv, int Nq, int Nk, int d, int cus, int occ, int& seq_dq,
                 int& seq_dkdv) {
   (void)d;
   const long long bt = fa::BWD_BT;
   const long long dq_items = (long long)B * H * ((Nq + bt - 1) / bt);
   const long long dkdv_items = (long long)B * Hkv * ((Nk + bt - 1) / bt);
-  seq_dq = ((B * H) % 8 == 0 && fa::bwd_head_sequential(dq_items, cus, occ)) ? 1 : 0;
-  seq_dkdv = ((B * Hkv) % 8 == 0 && fa::bwd_head_sequential(dkdv_items, cus, occ)) ? 1 : 0;
+  seq_dq = ((B * H) % 8 == 0 && fa::head_sequential(dq_items, cus, occ)) ? 1 : 0;
+  seq_dkdv = ((B * Hkv) % 8 == 0 && fa::head_sequential(dkdv_items, cus, occ)) ? 1 : 0;
 }
 
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -342,8 +345,10 @@ int fa_fwd_tile_order(int Nq, int Nk, int BH, int d, int dtype, int mask_kind, i
     occ = fa::fwd_occupancy(d, fa::FWD_BN, causal,
                             dtype == FA_DTYPE_F16 ? fa::DTYPE_F16 : fa::DTYPE_BF16);
   }
-  return fa::fwd_pair_tiles(Nq, Nk, d, BH, causal, cus, occ) ? FA_FWD_ORDER_PAIRED
-                                                             : FA_FWD_ORDER_HEAVY_FIRST;
+  if (fa::fwd_pair_tiles(Nq, Nk, d, BH, causal, cus, occ)) return FA_FWD_ORDER_PAIRED;
+  if (fa::fwd_head_sequential(Nq, Nk, d, BH, causal, cus, occ))
+    return FA_FWD_ORDER_HEAD_SEQUENTIAL;
+  return FA_FWD_ORDER_HEAVY_FIRST;
 }
 
 int fa_bwd_tile_order(int B, int H, int Hkv, int Nq, int Nk, int d, int cus, int occ) {

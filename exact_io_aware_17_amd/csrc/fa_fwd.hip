@@ -56,6 +56,10 @@
 //    Flash Attention"; "Exercises", a common reference), every pair streams
 //    about ntiles+1 tiles' worth of blocks, and the pairs of a head read the
 //    same two blocks at a time, so K and V are fetched about once per XCD.
+//    On grids of 16 or more rounds of resident workgroups (and B*H a
+//    multiple of 8) each XCD instead runs its heads one after another, so
+//    only a few heads' K and V share its L2 at a time; the outputs are
+//    bitwise the same in every order.
 //  * Load balance: a host plan may cut a tile's key range into up to 16
 //    parts (64 when the query rows are a single tile) processed by
 //    different workgroups. Each part stores its partial
@@ -187,7 +191,13 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // is a multiple of 8, the items of a fixed set of heads, whose K and V
     // then share its L2.
     bh = blockIdx.x % BH;
-    const int rank = blockIdx.x / BH;
+    int rank = blockIdx.x / BH;
+    if (p.seq && plan.nitems == 0 && (BH & 7) == 0) {
+      // Head-sequential: XCD x takes the same heads (x, x+8, ...) but runs
+      // them one after another, heaviest tile first within a head.
+      bh = (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) / ntiles);
+      rank = (blockIdx.x >> 3) % ntiles;
+    }
     if (plan.nitems > 0) {
       const unsigned it = plan.item[rank];
       tile0 = (int)(it & 0x1ffu);

@@ -30,6 +30,10 @@ struct FwdParams {
   // Causal without a split plan: 1 if each workgroup takes the pair of
   // query tiles (ntiles-1-r, r) (fwd_pair_tiles), 0 for one tile each.
   int pair;
+  // One tile per workgroup, no split plan: 1 if each XCD runs its heads one
+  // after another (fwd_head_sequential), 0 for
+  // the item-major order.
+  int seq;
   // Split work items (used only with a plan of nitems > 0): per (b, h)
   // nslots partial states, each BM rows of unnormalised O (fp32) plus the
   // row max and both row sums, and one arrival counter per query tile.
@@ -125,7 +129,7 @@ struct BwdParams {
   float scale_log2;
   int causal;
   int diag;                // as FwdParams
-  // Work order of each gradient kernel (bwd_head_sequential): 0 tile-major
+  // Work order of each gradient kernel (head_sequential): 0 tile-major
   // (every XCD starts with the heaviest tiles of all its heads), 1 each XCD
   // runs its heads one after another.
   int seq_dq, seq_dkdv;
@@ -138,15 +142,22 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
-// Whether a backward kernel with `items` workgroups (heads a multiple of 8)
+// Whether a kernel with `items` workgroups over heads (a multiple of 8)
 // should run each XCD's heads one after another: when the grid is at least
 // 16 rounds of the cus * occ resident slots. The tile-major order then keeps
 // every head of an XCD streaming its operands at once, past the L2 and the
 // Infinity Cache, while the longest-first balance that the sequential order
-// gives up within an XCD matters little over that many rounds (measured:
-// 2 rounds -13 %, 4 rounds -4 %, 8 rounds -1 to -4 %, 16 rounds +4 to +13 %,
-// 32 rounds +13 to +31 %).
-bool bwd_head_sequential(long long items, int cus, int occ);
+// gives up within an XCD matters little over that many rounds. Measured on
+// the backward: 2 rounds -13 %, 4 rounds -4 %, 8 rounds -1 to -4 %,
+// 16 rounds +4 to +13 %, 32 rounds +13 to +31 %. On the forward at d = 128:
+// 4 to 8 causal rounds -3 to -21 %, non-causal +-1 %; 16 rounds +10 to
+// +36 %, 32 rounds +27 %.
+bool head_sequential(long long items, int cus, int occ);
+
+// The forward's order for one tile per workgroup and no split plan: each
+// XCD runs its heads one after another (head_sequential on BH * ntiles
+// workgroups, BH a multiple of 8) unless the causal tiles are paired.
+bool fwd_head_sequential(int N, int Nk, int d, int BH, bool causal, int cus, int occ);
 
 // fa_fwd_ex_noalloc's workspace: a device array of this many bytes per GPU
 // (fa_noalloc.hip). noalloc_scratch() returns the current device's copy

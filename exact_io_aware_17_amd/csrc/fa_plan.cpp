@@ -39,7 +39,7 @@ int fwd_tile_blocks(int N, int Nk, int t, bool causal, int bn) {
   return (int)((kend + bn - 1) / bn);
 }
 
-bool bwd_head_sequential(long long items, int cus, int occ) {
+bool head_sequential(long long items, int cus, int occ) {
   if (cus <= 0 || occ <= 0) return false;
   return items >= 16ll * cus * occ;
 }
@@ -49,6 +49,12 @@ bool fwd_pair_tiles(int N, int Nk, int d, int BH, bool causal, int cus, int occ)
   if (!causal || ntiles < 2 || Nk <= 0 || d <= 0 || BH <= 0 || cus <= 0 || occ <= 0) return false;
   if (2ll * Nk * d * 2 < FWD_L2_BYTES) return false;
   return (long long)BH * ((ntiles + 1) / 2) >= (long long)cus * occ;
+}
+
+bool fwd_head_sequential(int N, int Nk, int d, int BH, bool causal, int cus, int occ) {
+  if (N <= 0 || BH <= 0 || BH % 8 != 0) return false;
+  if (fwd_pair_tiles(N, Nk, d, BH, causal, cus, occ)) return false;
+  return head_sequential((long long)BH * ((N + FWD_BM - 1) / FWD_BM), cus, occ);
 }
 
 namespace {

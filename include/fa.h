@@ -75,7 +75,7 @@ struct ihipStream_t;
 typedef struct ihipStream_t* hipStream_t;
 #endif
 
-#define FA_ABI_VERSION 11
+#define FA_ABI_VERSION 12
 
 typedef enum {
   FA_OK = 0,
@@ -262,12 +262,16 @@ typedef enum {
   FA_FWD_ORDER_HEAVY_FIRST = 0,  /* one tile per workgroup, the tiles that see
                                     the most keys dispatched first; keys
                                     stream in ascending order */
-  FA_FWD_ORDER_PAIRED = 1        /* causal: workgroup r takes tile
+  FA_FWD_ORDER_PAIRED = 1,       /* causal: workgroup r takes tile
                                     ntiles-1-r (keys ascending) and then tile
                                     r (keys descending), so every workgroup
                                     streams about ntiles+1 tiles' worth of
                                     key blocks and those of one head read the
                                     same two key blocks at a time */
+  FA_FWD_ORDER_HEAD_SEQUENTIAL = 2 /* one tile per workgroup; each XCD (the
+                                    workgroups of one residue of the id mod 8)
+                                    runs its heads one after another, the
+                                    heaviest tile of a head first */
 } fa_fwd_order;
 
 /*
@@ -282,7 +286,12 @@ typedef enum {
  * the L2 cache of one XCD, and BH * ceil(Nq / 128) / 2 workgroups still fill
  * every resident slot: streaming every tile from key 0 then fetches K and V
  * again from memory in proportion to Nq, while pairs keep the fetched bytes
- * a constant multiple of the inputs.
+ * a constant multiple of the inputs. Otherwise the heads run one after
+ * another on each XCD when BH is a multiple of 8 and the BH * ceil(Nq / 128)
+ * workgroups are at least 16 rounds of the cus * occ resident slots, so that
+ * few heads' K and V share an XCD's L2 at a time; on smaller grids the tiles
+ * go out item-major (all heads' heaviest tiles first), which balances the
+ * last rounds. Outputs are bitwise the same in every order.
  * Returns an fa_fwd_order value, FA_ERR_INVALID_ARG for invalid arguments,
  * or FA_ERR_UNSUPPORTED for FA_DTYPE_F32.
  */

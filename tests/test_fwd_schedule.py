@@ -236,11 +236,20 @@ L2_BYTES = 4 << 20   # one XCD's L2 cache, the header's threshold
 def expected_order(Nq, Nk, BH, d, causal, cus, occ):
     """The header's rule: pairs under a causal mask when one head's K and V
     (2 * Nk * d two-byte elements) are at least one XCD's L2 and the pairs
-    still fill every resident slot."""
+    still fill every resident slot; else heads one after another per XCD when
+    B*H is a multiple of 8 and the grid is at least 16 rounds of slots."""
     ntiles = -(-Nq // BM)
     paired = (causal and ntiles >= 2 and 2 * Nk * d * 2 >= L2_BYTES
               and BH * (-(-ntiles // 2)) >= cus * occ)
-    return _lib.FA_FWD_ORDER_PAIRED if paired else _lib.FA_FWD_ORDER_HEAVY_FIRST
+    if paired:
+        return _lib.FA_FWD_ORDER_PAIRED
+    if BH % 8 == 0 and BH * ntiles >= 16 * cus * occ:
+        return _lib.FA_FWD_ORDER_HEAD_SEQUENTIAL
+    return _lib.FA_FWD_ORDER_HEAVY_FIRST
+
+
+_ORDER = {"heavy": _lib.FA_FWD_ORDER_HEAVY_FIRST, "paired": _lib.FA_FWD_ORDER_PAIRED,
+          "seq": _lib.FA_FWD_ORDER_HEAD_SEQUENTIAL}
 
 
 @pytest.mark.parametrize("Nq,Nk,BH,d,causal,cus,occ,want", [
@@ -256,11 +265,19 @@ def expected_order(Nq, Nk, BH, d, causal, cus, occ):
     (128, 1 << 20, 4096, 128, True, 256, 2, "heavy"), # a single tile
     (256, 8192, 512, 128, True, 256, 2, "paired"),    # Nq < Nk
     (4096, 4096, 16, 256, True, 256, 1, "paired"),    # d = 256: 4 MB at N = 4096
+    (2048, 2048, 512, 128, True, 256, 2, "seq"),      # 8192 workgroups: 16 rounds of 512
+    (2048, 2048, 504, 128, True, 256, 2, "heavy"),    # 8064: under 16 rounds
+    (2048, 2048, 516, 128, True, 256, 2, "heavy"),    # B*H not a multiple of 8
+    (4096, 4096, 256, 128, False, 256, 2, "seq"),     # no mask
+    (1024, 1024, 1024, 64, True, 256, 3, "heavy"),    # 8192 for 768 slots: 10.7 rounds
+    (1024, 1024, 2048, 64, True, 256, 3, "seq"),
+    (8192, 8192, 512, 128, True, 256, 2, "paired"),   # pairs first
+    (128, 1 << 16, 8192, 128, True, 256, 2, "seq"),   # single tiles, many heads
 ])
 def test_tile_order_rule(Nq, Nk, BH, d, causal, cus, occ, want):
     got = _lib.tile_order(Nq, BH, d, causal, Nk=Nk, cus=cus, occ=occ)
     assert got == expected_order(Nq, Nk, BH, d, causal, cus, occ)
-    assert got == (_lib.FA_FWD_ORDER_PAIRED if want == "paired" else _lib.FA_FWD_ORDER_HEAVY_FIRST)
+    assert got == _ORDER[want]
     # Strict causal orders like causal; fp16 like bf16.
     assert _lib.tile_order(Nq, BH, d, "strict" if causal else False, Nk=Nk, cus=cus, occ=occ) == got
     import torch
@@ -270,12 +287,13 @@ def test_tile_order_rule(Nq, Nk, BH, d, causal, cus, occ, want):
 def test_tile_order_sweep_matches_rule():
     for Nq in (128, 256, 1000, 4096, 8192, 12345, 16384):
         for Nk in (Nq, 2 * Nq, 70000):
-            for BH in (1, 8, 20, 64):
+            for BH in (1, 8, 20, 64, 256, 1000, 1024):
                 for d in (32, 64, 128, 256):
                     for occ in (1, 2, 3):
-                        got = _lib.tile_order(Nq, BH, d, True, Nk=Nk, cus=256, occ=occ)
-                        assert got == expected_order(Nq, Nk, BH, d, True, 256, occ), \
-                            (Nq, Nk, BH, d, occ)
+                        for causal in (True, False):
+                            got = _lib.tile_order(Nq, BH, d, causal, Nk=Nk, cus=256, occ=occ)
+                            assert got == expected_order(Nq, Nk, BH, d, causal, 256, occ), \
+                                (Nq, Nk, BH, d, occ, causal)
 
 
 def test_tile_order_argument_errors():
