@@ -55,6 +55,9 @@ PROBE_LIB = os.path.join(ROOT, "exact_io_aware_17_amd", "libfa_probe.so")
 FLUSH_BYTES = 512 * 2 ** 20  # > 8 x 4 MB of L2 + 256 MB of Infinity Cache
 SWEEP_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_causal_bh32d128_traffic_sweep.json")
 SWEEP_N = (1024, 2048, 4096, 8192, 16384)  # causal, B=2, H=16, d=128
+# causal d=128 bf16 batches of 16 or more rounds of workgroups, which run
+# each XCD's heads one after another: (B, H, N)
+LARGE_BATCHES = ((16, 32, 2048), (8, 32, 4096))
 KERNEL_SOURCES = [
     os.path.join(ROOT, "exact_io_aware_17_amd", "csrc", f)
     for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")
@@ -147,8 +150,9 @@ COPY_BYTES = 256 * 2 ** 20  # calibration copy: 256 MiB read + 256 MiB written
 def profile_run(w) -> int:
     """A short run for counter collection: a plain copy of known size three
     times, the forward kernel on the workload three times, then once at each
-    N of the traffic sweep (causal, B=2, H=16, d=128), then the naive
-    forward once on the workload, then one fa_bwd on the workload."""
+    N of the traffic sweep (causal, B=2, H=16, d=128) and once on each of
+    LARGE_BATCHES, then the naive forward once on the workload, then one
+    fa_bwd on the workload."""
     import torch
     import exact_io_aware_17_amd as fa
     from exact_io_aware_17_amd import workloads as W
@@ -175,6 +179,15 @@ def profile_run(w) -> int:
         torch.cuda.synchronize()
         del qs, ks, vs
         print(f"profile run: sweep N={n} done", flush=True)
+    for B, H, n in LARGE_BATCHES:
+        ws = W.with_shape(W.BY_ID[5], B=B, H=H, N=n)
+        xs = W.make_inputs(ws)
+        qs, ks, vs = (xs[c].to(dev) for c in ("q", "k", "v"))
+        del xs
+        fa.fwd(qs, ks, vs, causal=True, scale=ws.scale)
+        torch.cuda.synchronize()
+        del qs, ks, vs
+        print(f"profile run: batch B={B} H={H} N={n} done", flush=True)
     naive_forward(q, k, v, w.scale, w.causal)
     torch.cuda.synchronize()
     print("profile run: naive forward done", flush=True)
@@ -215,8 +228,9 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
         copy = [v for i, n, v in rows
                 if i < first_fwd and FWD_KERNEL_TAG not in n and v >= 0.25 * COPY_BYTES / 1024]
         fwd = [v for _, n, v in rows if FWD_KERNEL_TAG in n]
-        if not copy or len(fwd) != 3 + len(SWEEP_N):
-            print(f"{counter}: expected copy readings and {3 + len(SWEEP_N)} forward "
+        nfwd = 3 + len(SWEEP_N) + len(LARGE_BATCHES)
+        if not copy or len(fwd) != nfwd:
+            print(f"{counter}: expected copy readings and {nfwd} forward "
                   f"dispatches, got {len(copy)} and {len(fwd)}", file=sys.stderr)
             return 1
         scale = COPY_BYTES / (sorted(copy)[len(copy) // 2] * 1024.0)
@@ -229,7 +243,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
         out[key + "_kib_raw"] = wl
         out[key + "_scale"] = scale
         out[key + "_bytes_per_launch"] = wl * 1024.0 * scale
-        per_key[key] = [v * 1024.0 * scale for v in fwd[3:]]
+        per_key[key] = [v * 1024.0 * scale for v in fwd[3:]]  # sweep, then batches
     out["hbm_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
     out["naive_hbm_bytes"] = out["naive_fetch_bytes"] + out["naive_write_bytes"]
     out["naive_over_fa_fwd"] = out["naive_hbm_bytes"] / out["hbm_bytes_per_launch"]
@@ -240,6 +254,14 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> int:
                               "write_bytes": per_key["write"][i], "hbm_bytes": meas,
                               "algorithmic_bytes": alg, "ratio": meas / alg,
                               "s_p_roundtrip_bytes": 2 * 2 * 16 * W.score_matrix_bytes(n, 2)})
+    sweep["large_batches"] = []
+    for j, (B, H, n) in enumerate(LARGE_BATCHES):
+        i = len(SWEEP_N) + j
+        alg = W.fwd_bytes(B, H, n, 128, 2)
+        meas = per_key["fetch"][i] + per_key["write"][i]
+        sweep["large_batches"].append({"B": B, "H": H, "N": n, "fetch_bytes": per_key["fetch"][i],
+                                       "write_bytes": per_key["write"][i], "hbm_bytes": meas,
+                                       "algorithmic_bytes": alg, "ratio": meas / alg})
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     with open(SWEEP_FILE, "w") as f:

@@ -54,10 +54,11 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     copy = bench.COPY_BYTES / 1024.0
     # FETCH_SIZE reads half the bytes (scale 2), WRITE_SIZE all of them (scale 1)
     fetch_rows = _profile_dispatches(copy / 2, [60000.0, 61000.0, 70000.0],
-                                     [100.0, 200.0, 300.0, 400.0, 500.0], [1000.0, 2000.0],
-                                     [80007.0, 90000.0])
+                                     [100.0, 200.0, 300.0, 400.0, 500.0, 600.0, 700.0],
+                                     [1000.0, 2000.0], [80007.0, 90000.0])
     write_rows = _profile_dispatches(copy, [30000.0, 30000.0, 30000.0],
-                                     [10.0, 20.0, 30.0, 40.0, 50.0], [500.0], [3.0, 3.0])
+                                     [10.0, 20.0, 30.0, 40.0, 50.0, 60.0, 70.0], [500.0],
+                                     [3.0, 3.0])
     _write_counter_csv(str(tmp_path / "f" / "vm" / "1_counter_collection.csv"), "FETCH_SIZE",
                        fetch_rows)
     _write_counter_csv(str(tmp_path / "w" / "vm" / "1_counter_collection.csv"), "WRITE_SIZE",
@@ -81,13 +82,20 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert r0["hbm_bytes"] == pytest.approx(100.0 * 2048 + 10.0 * 1024)
     # algorithmic bytes of causal B=2, H=16, N=1024, d=128 bf16: Q, K, V, O and lse
     assert r0["algorithmic_bytes"] == 4 * 2 * 16 * 1024 * 128 * 2 + 2 * 16 * 1024 * 4
+    # the large batches follow the sweep's dispatches, in order
+    assert [(r["B"], r["H"], r["N"]) for r in s["large_batches"]] == list(bench.LARGE_BATCHES)
+    lb = s["large_batches"][0]
+    assert lb["hbm_bytes"] == pytest.approx(600.0 * 2048 + 60.0 * 1024)
+    B, H, N = bench.LARGE_BATCHES[0]
+    assert lb["algorithmic_bytes"] == 4 * B * H * N * 128 * 2 + B * H * N * 4
 
 
 def test_traffic_summary_rejects_missing_dispatches(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     monkeypatch.setattr(bench, "SWEEP_FILE", str(tmp_path / "sweep.json"))
     copy = bench.COPY_BYTES / 1024.0
-    rows = _profile_dispatches(copy, [1.0, 1.0], [1.0] * len(bench.SWEEP_N), [])
+    rows = _profile_dispatches(copy, [1.0, 1.0],
+                               [1.0] * (len(bench.SWEEP_N) + len(bench.LARGE_BATCHES)), [])
     _write_counter_csv(str(tmp_path / "f" / "a_counter_collection.csv"), "FETCH_SIZE", rows)
     _write_counter_csv(str(tmp_path / "w" / "a_counter_collection.csv"), "WRITE_SIZE", rows)
     assert bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "cmd") == 1
