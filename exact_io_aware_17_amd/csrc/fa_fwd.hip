@@ -400,10 +400,12 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
     // reference moves to the row's block max if that lies more than TAU above
     // it (rescaling the accumulators once), and the block's p are recomputed.
     x8 pf[KC];
-    float rs, lbf_blk;
+    // rs: this block's fp32 sum (from -0, so the first addition is exact and
+    // needs no instruction); lbf_new: l_bf with this block's rounded p added.
+    float rs, lbf_new;
     auto probabilities = [&](float m_use) {
-      rs = 0.f;
-      lbf_blk = 0.f;
+      rs = -0.f;
+      lbf_new = l_bf;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         u32x4 w;
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r + 1], scl, -m_use));
           w[e] = E::pack(p0, p1);
           rs += p0 + p1;
-          lbf_blk = E::add_pair(w[e], lbf_blk);
+          lbf_new = E::add_pair(w[e], lbf_new);
         }
         pf[kc] = __builtin_bit_cast(x8, w);
       }
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(NW * 64, fwd_wg_per_cu(D, BN)) void fwd_kernel(FwdP
       }
     }
     l_run += rs;
-    l_bf += lbf_blk;
+    l_bf = lbf_new;
 
     __builtin_amdgcn_s_setprio(FA_PRIO_MFMA);
     // ---- O^T += V^T P^T ----
