@@ -582,12 +582,63 @@ def mfma_probe(dev, stream, flops_target, reps, warmup=3):
             "per_launch_events": per}
 
 
+def hbm_probe(dev, stream, reps=10, warmup=3, blocks=64):
+    """The HBM -> LDS rate this device sustains: libfa_probe's streaming
+    kernel (the forward's buffer-load-to-LDS path and two-stage ring, two
+    workgroups per CU), each workgroup reading `blocks` 32 KB blocks."""
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it with "
+                           "python -m exact_io_aware_17_amd.build")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fa_probe_stream_lds.restype = ctypes.c_int
+    lib.fa_probe_stream_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_stream_lds_bytes.restype = ctypes.c_double
+    lib.fa_probe_stream_lds_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = lib.fa_probe_stream_lds_bytes(wgs, blocks)
+    src = torch.ones(int(nbytes) // 2, dtype=torch.bfloat16, device=dev)
+    sums = torch.empty(wgs, dtype=torch.float32, device=dev)
+
+    def once():
+        r = lib.fa_probe_stream_lds(ctypes.c_void_p(src.data_ptr()), wgs, blocks,
+                                    ctypes.c_void_p(sums.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"fa_probe_stream_lds returned {r}")
+
+    for _ in range(warmup):
+        once()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        once()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del src
+    return {"what": "HBM -> LDS streaming alone: 16-byte buffer loads into LDS, two 32 KB "
+                    "stages, two workgroups of 4 waves per CU (the forward's K/V path)",
+            "bytes": int(nbytes), "ms": round(ms, 5), "gb_s": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def decode_shapes(dev, stream):
     """Decode on a batch of sequences and on one long sequence (few K/V heads
     over a 131k-token cache, where a tile's key range is split in up to 64
-    parts)."""
-    return {"batch": decode_comparison(dev, stream),
-            "one_long_sequence": decode_comparison(dev, stream, B=1, Nk=131072)}
+    parts), beside the HBM -> LDS streaming rate of the device."""
+    out = {"batch": decode_comparison(dev, stream),
+           "one_long_sequence": decode_comparison(dev, stream, B=1, Nk=131072),
+           "hbm_probe": hbm_probe(dev, stream)}
+    for key in ("batch", "one_long_sequence"):
+        for name in ("fa_fwd_ex", "fa_fwd_ex_split"):
+            out[key][name]["frac_of_probe"] = round(
+                out[key][name]["gb_s"] / out["hbm_probe"]["gb_s"], 4)
+    return out
 
 
 def decode_comparison(dev, stream, B=8, H=32, Hkv=8, Nk=32768, d=128, reps=20):

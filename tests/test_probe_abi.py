@@ -1,6 +1,7 @@
-"""libfa_probe (the matrix-core rate probe the benchmark measures beside the
-forward) loads, exports what include/fa_probe.h declares, rejects bad
-arguments before any HIP call, and states its FLOPs per launch."""
+"""libfa_probe (the matrix-core and HBM -> LDS rate probes the benchmark
+measures beside the forward and the decode) loads, exports what
+include/fa_probe.h declares, rejects bad arguments before any HIP call, and
+states its FLOPs and bytes per launch."""
 import ctypes
 import os
 import re
@@ -16,6 +17,11 @@ def _load():
     lib.fa_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_mfma_bf16_flops.restype = ctypes.c_double
     lib.fa_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.fa_probe_stream_lds.restype = ctypes.c_int
+    lib.fa_probe_stream_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.fa_probe_stream_lds_bytes.restype = ctypes.c_double
+    lib.fa_probe_stream_lds_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
     return lib
 
 
@@ -23,7 +29,8 @@ def test_exports_what_the_header_declares():
     with open(os.path.join(ROOT, "include", "fa_probe.h")) as f:
         text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_probe_\w+)\s*\(", text)))
-    assert names == ["fa_probe_mfma_bf16", "fa_probe_mfma_bf16_flops"]
+    assert names == ["fa_probe_mfma_bf16", "fa_probe_mfma_bf16_flops", "fa_probe_stream_lds",
+                     "fa_probe_stream_lds_bytes"]
     lib = _load()
     for n in names:
         assert hasattr(lib, n), n
@@ -36,6 +43,13 @@ def test_bad_arguments_are_rejected_before_launch():
     assert lib.fa_probe_mfma_bf16(-4, 10, sink, None) == -1
     assert lib.fa_probe_mfma_bf16(512, 0, sink, None) == -1
     assert lib.fa_probe_mfma_bf16(512, 10, None, None) == -1
+    src = ctypes.c_void_p(0x20000000)
+    assert lib.fa_probe_stream_lds(None, 512, 8, sink, None) == -1
+    assert lib.fa_probe_stream_lds(src, 512, 8, None, None) == -1
+    assert lib.fa_probe_stream_lds(src, 0, 8, sink, None) == -1
+    assert lib.fa_probe_stream_lds(src, 512, 0, sink, None) == -1
+    assert lib.fa_probe_stream_lds(src, (1 << 20) + 1, 8, sink, None) == -1
+    assert lib.fa_probe_stream_lds(src, 512, (1 << 16) + 1, sink, None) == -1
 
 
 def test_flops_per_launch():
@@ -43,3 +57,9 @@ def test_flops_per_launch():
     # 4 waves per workgroup, 4 MFMAs per round, 32 x 32 x 16 x 2 FLOPs each
     assert lib.fa_probe_mfma_bf16_flops(512, 512) == 512 * 4 * 512 * 4 * 32 * 32 * 16 * 2
     assert lib.fa_probe_mfma_bf16_flops(0, 5) == 0.0
+
+
+def test_stream_bytes_per_launch():
+    lib = _load()
+    assert lib.fa_probe_stream_lds_bytes(512, 64) == 512 * 64 * 32768
+    assert lib.fa_probe_stream_lds_bytes(512, 0) == 0.0
