@@ -9,8 +9,10 @@ batch (value = forward TFLOP/s at 4*B*H*N^2*d/2 FLOPs). The backward pass is
 timed the same way and reported beside it ("bwd"), together with one full
 forward+backward pass ("fwd_bwd_step"), fa_fwd_ex (split-KV) is compared with
 fa_fwd on a grid too small to fill the GPU ("split_kv") and on decode, one
-query row per head over a long cache, against the HBM peak ("decode"), and a
-naive forward that materialises S and P in device memory (PyTorch matmul +
+query row per head over a long cache, against the HBM peak and the rate of
+the forward's HBM -> LDS load path alone ("decode"), the forward and the
+backward run at large batches whose grids take the head-sequential order
+("large_batch"), and a naive forward that materialises S and P in device memory (PyTorch matmul +
 softmax, the comparison path, not part of libfa) is timed on the same inputs
 ("naive").
 
@@ -494,6 +496,56 @@ def split_kv_comparison(dev, stream, B=1, H=2, N=16384, d=128, reps=10):
     return res
 
 
+def large_batch_comparison(dev, stream, reps=10, settle_ms=100.0):
+    """Large batches, whose grids of 16 or more rounds of resident workgroups
+    run each XCD's heads one after another (fa_fwd_tile_order and
+    fa_bwd_tile_order report the orders): the forward at three shapes and the
+    backward at one, bf16, d = 128, inputs drawn on the device. Each call is
+    timed after settle_ms of the same calls (the clock settle of the main
+    measurement)."""
+    import torch
+    import exact_io_aware_17_amd as fa
+    from exact_io_aware_17_amd import workloads as W
+
+    names = {fa.FA_FWD_ORDER_HEAVY_FIRST: "heavy-first", fa.FA_FWD_ORDER_PAIRED: "paired",
+             fa.FA_FWD_ORDER_HEAD_SEQUENTIAL: "head-sequential"}
+    res = {}
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+
+    def timed(f):
+        settle_clock(f, settle_ms, stream, group=5)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for B, H, N, causal, bwd in ((16, 32, 2048, True, False), (8, 32, 4096, True, True),
+                                 (8, 32, 4096, False, False)):
+        d = 128
+        g = torch.Generator(device=dev).manual_seed(17100 + N)
+        q, k, v = (torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(3))
+        key = f"{'causal' if causal else 'non-causal'} B={B} H={H} N={N} d={d}"
+        ms = timed(lambda: fa.fwd(q, k, v, causal=causal))
+        ent = {"tile_order": names[fa.tile_order(N, B * H, d, causal)], "fwd_ms": round(ms, 5),
+               "fwd_tflops": round(W.fwd_flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12, 1)}
+        if bwd:
+            o, lse = fa.fwd(q, k, v, causal=causal)
+            do = torch.randn(B, H, N, d, generator=g, device=dev).to(torch.bfloat16)
+            ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=causal))
+            ent["bwd_order"] = fa.bwd_tile_order(B, H, N, d)
+            ent["bwd_ms"] = round(ms, 5)
+            ent["bwd_tflops"] = round(W.bwd_flops(B, H, N, d, causal) / (ms * 1e-3) / 1e12, 1)
+            del o, lse, do
+        res[key] = ent
+        del q, k, v
+    return res
+
+
 def timed_region(fn, steps, stream):
     """Mean ms per launch of `steps` launches back to back between two events."""
     import torch
@@ -892,6 +944,7 @@ def main() -> int:
         if not args.no_split_kv:
             out["split_kv"] = split_kv_comparison(dev, stream)
             out["decode"] = decode_shapes(dev, stream)
+            out["large_batch"] = large_batch_comparison(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
 
