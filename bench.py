@@ -10,9 +10,9 @@ timed the same way and reported beside it ("bwd"), together with one full
 forward+backward pass ("fwd_bwd_step"), fa_fwd_ex (split-KV) is compared with
 fa_fwd on a grid too small to fill the GPU ("split_kv") and on decode, one
 query row per head over a long cache, against the HBM peak and the rate of
-the forward's HBM -> LDS load path alone ("decode"), the forward and the
-backward run at large batches whose grids take the head-sequential order
-("large_batch"), and a naive forward that materialises S and P in device memory (PyTorch matmul +
+the forward's HBM -> LDS load path alone ("decode"), with --large-batch the
+forward and the backward at large batches whose grids take the
+head-sequential order ("large_batch"), and a naive forward that materialises S and P in device memory (PyTorch matmul +
 softmax, the comparison path, not part of libfa) is timed on the same inputs
 ("naive").
 
@@ -736,6 +736,10 @@ def main() -> int:
                          "the timed region starts at the device's sustained clock (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--large-batch", action="store_true",
+                    help="also time the forward and backward at large batches (the "
+                         "head-sequential orders); off by default, since those launches of "
+                         "the metric kernel would change its average in a kernel trace")
     ap.add_argument("--no-split-kv", action="store_true",
                     help="skip the split-KV comparison (it launches the forward kernel "
                          "at another shape)")
@@ -944,6 +948,7 @@ def main() -> int:
         if not args.no_split_kv:
             out["split_kv"] = split_kv_comparison(dev, stream)
             out["decode"] = decode_shapes(dev, stream)
+        if args.large_batch:
             out["large_batch"] = large_batch_comparison(dev, stream)
         out["naive"] = naive_comparison(w, q, k, v, o, stream)
         out["naive"]["speedup_fa_fwd"] = round(out["naive"]["ms"] / ms_step, 2)
