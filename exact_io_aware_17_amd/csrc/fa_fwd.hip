@@ -103,9 +103,11 @@ constexpr float lag_tau() { return std::is_same<T, _Float16>::value ? 8.0f : 32.
 #define FA_FWD_WG_PER_CU 3
 #endif
 
-// Resident workgroups per CU the register budget is sized for: at D = 256 the
-// Q^T fragments and output accumulators alone take 192 registers per lane;
-// with 64-key blocks D = 128 needs 202 registers and D = 96 171.
+// Resident workgroups per CU the register budget is sized for (a lower bound
+// for the compiler: what fits decides the occupancy). At D = 256 the Q^T
+// fragments and output accumulators alone take 192 registers per lane; with
+// 64-key blocks D = 128 takes 190 (two workgroups per CU) and D = 96 160
+// (three); D = 64 fits 128 (four) and D = 32 96 (five).
 constexpr int fwd_wg_per_cu(int D, int BN) {
   return D == 256 ? 1 : ((D == 128 || D == 96) && BN == 64 ? 2 : FA_FWD_WG_PER_CU);
 }

@@ -31,8 +31,7 @@ struct FwdParams {
   // query tiles (ntiles-1-r, r) (fwd_pair_tiles), 0 for one tile each.
   int pair;
   // One tile per workgroup, no split plan: 1 if each XCD runs its heads one
-  // after another (fwd_head_sequential), 0 for
-  // the item-major order.
+  // after another (fwd_head_sequential), 0 for the item-major order.
   int seq;
   // Split work items (used only with a plan of nitems > 0): per (b, h)
   // nslots partial states, each BM rows of unnormalised O (fp32) plus the
